@@ -1,0 +1,155 @@
+/*
+ * lsd_radix_sort.h -- C ABI of the MI355X (gfx950) LSD radix sort library.
+ *
+ * The method: least-significant-digit radix sort.  Each pass histograms one
+ * b-bit digit, exclusive-scans the 2^b bucket counts into base offsets and
+ * stably scatters the keys (and payload); passes go from the low digit to the
+ * high digit, ping-ponging between two buffers (CUDA Handbook ch.16 "Radix
+ * Sort", the three per-pass steps; DSA CUDA from first principles ch.13,
+ * section 13.3; gpu.rocks "The Whole Sort").
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates, frees and synchronises nothing: every call validates its
+ *    arguments on the host, enqueues its kernels on `stream` (a hipStream_t;
+ *    NULL = the null stream) and returns.
+ *  - Inputs are never written (sorting is out of place; 100 Days of GPU,
+ *    Day 35, "Pitfalls").  Outputs must not overlap inputs, each other or the
+ *    workspace (LRS_ERR_ALIASING).
+ *  - Data pointers are naturally aligned for their element type; the
+ *    workspace is 256-byte aligned (torch allocations are); otherwise
+ *    LRS_ERR_ALIGNMENT.
+ *  - The caller provides scratch device memory (`workspace`) of at least the
+ *    size the matching *_workspace_size() call returns; its contents on entry
+ *    do not matter and on return are unspecified.  Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - The result of a sort is unique: a stable sort by the key, ties in input
+ *    order, payload travelling with its key.
+ *  - Return value: LRS_OK or an lrs_status code.  Argument errors are reported
+ *    before anything is enqueued.  LRS_ERR_HIP means a kernel launch was
+ *    rejected by the runtime; faults during execution surface at the caller's
+ *    next synchronisation.  No C++ exception crosses this boundary.
+ */
+#ifndef LSD_RADIX_SORT_H
+#define LSD_RADIX_SORT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lrs_status {
+    LRS_OK = 0,
+    LRS_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    LRS_ERR_BIT_RANGE = 2,           /* begin_bit/end_bit outside 0 <= begin < end <= key width */
+    LRS_ERR_DIGIT_BITS = 3,          /* digit_bits not 1, 2, 4 or 8 */
+    LRS_ERR_SIZE = 4,                /* element count or shape beyond the supported limit */
+    LRS_ERR_ALIASING = 5,            /* an output overlaps an input, another output or the workspace */
+    LRS_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the *_workspace_size() figure */
+    LRS_ERR_DTYPE = 7,               /* dtype not LRS_DTYPE_FP16 / LRS_DTYPE_BF16 */
+    LRS_ERR_HIP = 8,                 /* the HIP runtime rejected a launch or query */
+    LRS_ERR_ALIGNMENT = 9            /* a pointer is not aligned as required (see below) */
+} lrs_status;
+
+#define LRS_DTYPE_FP16 0
+#define LRS_DTYPE_BF16 1
+
+/* Largest u32 sort: n < 2^32 elements.  Largest segmented row: n < 2^30
+ * (FlagTree PR #1084 caps one row at 2^30 elements). */
+#define LRS_MAX_KEYS 0xFFFFFFFFull
+#define LRS_MAX_ROW_LEN ((1ull << 30) - 1ull)
+
+/*
+ * Bytes of workspace radix_sort_keys (with_values = 0) or radix_sort_pairs
+ * (with_values = 1) needs for these arguments.  Returns 0 for arguments the
+ * sort would reject, and for n == 0.
+ */
+size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int digit_bits,
+                                 int with_values);
+
+/*
+ * Stable LSD sort of n u32 keys by the bit window [begin_bit, end_bit),
+ * digit_bits (b) bits per pass, ceil((end_bit - begin_bit) / b) passes, low
+ * digit first; the last pass is narrower when b does not divide the window
+ * (CUDA Handbook ch.16, the pass and driver; b in {1, 2, 4, 8} as that page
+ * allows).  Bits outside the window travel with the key but do not order it:
+ * keys equal inside the window keep their input order.
+ *   keys_in   [n] u32, read only          keys_out [n] u32, written
+ *   0 <= begin_bit < end_bit <= 32; n < 2^32; n == 0 is a no-op.
+ */
+int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int begin_bit,
+                    int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * As radix_sort_keys, carrying one u32 payload per key: vals_out[i] is the
+ * payload of the key that lands at keys_out[i] (100 Days of GPU, Day 35,
+ * "Exercise": the payload rides along with every move of its key).
+ *   vals_in [n] u32, read only            vals_out [n] u32, written
+ */
+int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+                     uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace segmented_row_sort needs; 0 for rejected arguments or empty input. */
+size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits);
+
+/*
+ * Sort each row of a row-major rows x n matrix of fp16 or bf16 values
+ * independently, ascending or descending, returning the sorted values and the
+ * int64 column each came from (FlagTree PR #1084: the radix sort behind
+ * torch-style sort over the last dimension, with an arange column index as
+ * payload).  Keys are the 16-bit patterns through an order-preserving map
+ * (100 Days of GPU, Day 35, "Pitfalls"): negative patterns are complemented,
+ * non-negative ones get the sign bit set; descending uses the complement of
+ * that key, so equal values keep their input order in both directions.
+ * -0 sorts immediately before +0 ascending (after it descending); NaNs sort by
+ * pattern beyond the infinities.  Passes: 16 / digit_bits.
+ *   vals_in  [rows][n] u16 patterns, read only
+ *   vals_out [rows][n] u16 patterns, written (the input patterns, permuted)
+ *   idx_out  [rows][n] int64 column indices, written
+ *   dtype: LRS_DTYPE_FP16 or LRS_DTYPE_BF16; descending: 0 or 1
+ *   rows >= 0, 0 <= n <= LRS_MAX_ROW_LEN; rows * n < 2^40.
+ */
+int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx_out,
+                       int64_t rows, int64_t n, int dtype, int descending, int digit_bits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The per-pass digit counts of radix_sort_keys' first kernel: all passes'
+ * histograms from one read of the keys (FlagTree PR #1084, step 2 "Before":
+ * one kernel counts every pass).  hist_out[p * 2^b + d] = number of keys
+ * whose pass-p digit is d.  hist_out is a device array of
+ * ceil((end_bit - begin_bit) / b) * 2^b u32, 16-byte aligned, written (not
+ * accumulated).
+ */
+int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit,
+                                int digit_bits, uint32_t *hist_out, void *stream);
+
+/* Copy `bytes` bytes from src to dst with a plain streaming kernel (the
+ * bandwidth yardstick of 100 Days of GPU, Day 35, "Results", the copy row).
+ * Both pointers 16-byte aligned, non-overlapping. */
+int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
+
+/*
+ * Kernel timing for measurement.  After radix_sort_timing_begin(), every
+ * kernel the library enqueues is bracketed by HIP events on its stream.
+ * radix_sort_timing_end() waits for those events and reports, per kernel kind
+ * (0 = workspace clear, 1 = digit histogram, 2 = sweep/scatter pass,
+ * 3 = copy probe), the summed milliseconds and the number of launches, then
+ * stops recording.  Arrays have 4 entries.  At most 65536 launches are timed.
+ * Not thread-safe; for benchmarking only.
+ */
+int radix_sort_timing_begin(void);
+int radix_sort_timing_end(double *ms_by_kind, int *launches_by_kind);
+
+/* Static description of a status code; never NULL. */
+const char *radix_sort_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSD_RADIX_SORT_H */

@@ -1,0 +1,229 @@
+"""MI355X (gfx950) LSD radix sort: thin Python binding over the C ABI.
+
+Every step of every sort runs in the HIP kernels of ``liblsd_radix_sort.so``;
+this module only checks tensor shapes/dtypes, allocates outputs and the
+workspace with torch, and passes raw device pointers and the current HIP
+stream.  The entry points have the C ABI's names (include/lsd_radix_sort.h):
+
+    radix_sort_keys(keys, begin_bit=0, end_bit=32, digit_bits=8)
+    radix_sort_pairs(keys, values, begin_bit=0, end_bit=32, digit_bits=8)
+    segmented_row_sort(x, descending=False, digit_bits=8)
+    radix_sort_digit_histograms(keys, begin_bit, end_bit, digit_bits)
+
+u32 data is accepted as torch.uint32 or torch.int32 (bit patterns); outputs
+have the input's dtype.  There is no CPU fallback: without the built library or
+a GPU these calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblsd_radix_sort.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lsd_radix_sort.h")
+
+LRS_OK = 0
+LRS_DTYPE_FP16 = 0
+LRS_DTYPE_BF16 = 1
+STATUS_NAMES = {
+    0: "LRS_OK", 1: "LRS_ERR_NULL_POINTER", 2: "LRS_ERR_BIT_RANGE", 3: "LRS_ERR_DIGIT_BITS",
+    4: "LRS_ERR_SIZE", 5: "LRS_ERR_ALIASING", 6: "LRS_ERR_WORKSPACE_TOO_SMALL", 7: "LRS_ERR_DTYPE",
+    8: "LRS_ERR_HIP", 9: "LRS_ERR_ALIGNMENT",
+}
+_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9}
+
+_lib = None
+
+
+class RadixSortError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+class RadixSortArgumentError(RadixSortError, ValueError):
+    pass
+
+
+def load_library():
+    """Load the in-tree HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m lsd_radix_sort_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, u64, i64, c_int, szt = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.radix_sort_workspace_size.argtypes = [u64, c_int, c_int, c_int, c_int]
+    lib.radix_sort_workspace_size.restype = szt
+    lib.radix_sort_keys.argtypes = [P, P, u64, c_int, c_int, c_int, P, szt, P]
+    lib.radix_sort_keys.restype = c_int
+    lib.radix_sort_pairs.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, P, szt, P]
+    lib.radix_sort_pairs.restype = c_int
+    lib.segmented_row_sort_workspace_size.argtypes = [i64, i64, c_int]
+    lib.segmented_row_sort_workspace_size.restype = szt
+    lib.segmented_row_sort.argtypes = [P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P]
+    lib.segmented_row_sort.restype = c_int
+    lib.radix_sort_digit_histograms.argtypes = [P, u64, c_int, c_int, c_int, P, P]
+    lib.radix_sort_digit_histograms.restype = c_int
+    lib.radix_sort_copy_probe.argtypes = [P, P, szt, P]
+    lib.radix_sort_copy_probe.restype = c_int
+    lib.radix_sort_timing_begin.argtypes = []
+    lib.radix_sort_timing_begin.restype = c_int
+    lib.radix_sort_timing_end.argtypes = [P, P]
+    lib.radix_sort_timing_end.restype = c_int
+    lib.radix_sort_status_string.argtypes = [c_int]
+    lib.radix_sort_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().radix_sort_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != LRS_OK:
+        if status in _VALUE_ERRORS:
+            raise RadixSortArgumentError(status, what)
+        raise RadixSortError(status, what)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _u32_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in (torch.uint32, torch.int32):
+        raise ValueError(f"{name} must be uint32 or int32, got {t.dtype}")
+    if t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D tensor")
+    return t
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def radix_sort_workspace_size(n: int, begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8,
+                              with_values: bool = False) -> int:
+    return int(load_library().radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, int(with_values)))
+
+
+def segmented_row_sort_workspace_size(rows: int, n: int, digit_bits: int = 8) -> int:
+    return int(load_library().segmented_row_sort_workspace_size(rows, n, digit_bits))
+
+
+def radix_sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Stable LSD sort of u32 keys by bits [begin_bit, end_bit); returns the sorted keys."""
+    lib = load_library()
+    keys = _u32_tensor(keys, "keys")
+    n = keys.numel()
+    if out is None:
+        out = torch.empty_like(keys)
+    if workspace is None:
+        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 0), keys.device)
+    _check(lib.radix_sort_keys(_ptr(keys), _ptr(out), n, begin_bit, end_bit, digit_bits,
+                               _ptr(workspace), workspace.numel(), _stream(keys)), "radix_sort_keys")
+    return out
+
+
+def radix_sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+                     digit_bits: int = 8, keys_out: torch.Tensor | None = None,
+                     values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Stable LSD sort of u32 keys carrying u32 values; returns (keys, values)."""
+    lib = load_library()
+    keys = _u32_tensor(keys, "keys")
+    values = _u32_tensor(values, "values")
+    n = keys.numel()
+    if values.numel() != n:
+        raise ValueError("keys and values differ in length")
+    if keys_out is None:
+        keys_out = torch.empty_like(keys)
+    if values_out is None:
+        values_out = torch.empty_like(values)
+    if workspace is None:
+        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 1), keys.device)
+    _check(lib.radix_sort_pairs(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, begin_bit,
+                                end_bit, digit_bits, _ptr(workspace), workspace.numel(), _stream(keys)),
+           "radix_sort_pairs")
+    return keys_out, values_out
+
+
+def segmented_row_sort(x: torch.Tensor, descending: bool = False, digit_bits: int = 8,
+                       values_out: torch.Tensor | None = None, indices_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """Sort every row of a 2-D fp16/bf16 GPU tensor; returns (values, int64 column indices)."""
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if x.dtype == torch.float16:
+        dtype = LRS_DTYPE_FP16
+    elif x.dtype == torch.bfloat16:
+        dtype = LRS_DTYPE_BF16
+    else:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    rows, n = x.shape
+    if values_out is None:
+        values_out = torch.empty_like(x)
+    if indices_out is None:
+        indices_out = torch.empty((rows, n), dtype=torch.int64, device=x.device)
+    if workspace is None:
+        workspace = _workspace(lib.segmented_row_sort_workspace_size(rows, n, digit_bits), x.device)
+    _check(lib.segmented_row_sort(_ptr(x), _ptr(values_out), _ptr(indices_out), rows, n, dtype,
+                                  int(descending), digit_bits, _ptr(workspace), workspace.numel(),
+                                  _stream(x)), "segmented_row_sort")
+    return values_out, indices_out
+
+
+def radix_sort_digit_histograms(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+                                digit_bits: int = 8) -> torch.Tensor:
+    """All passes' digit counts from one read of the keys: int32 [passes, 2^b] (u32 counts)."""
+    lib = load_library()
+    keys = _u32_tensor(keys, "keys")
+    passes = -(-(end_bit - begin_bit) // digit_bits) if end_bit > begin_bit else 0
+    hist = torch.empty((max(passes, 1), 1 << digit_bits), dtype=torch.int32, device=keys.device)
+    _check(lib.radix_sort_digit_histograms(_ptr(keys), keys.numel(), begin_bit, end_bit, digit_bits,
+                                           _ptr(hist), _stream(keys)), "radix_sort_digit_histograms")
+    return hist
+
+
+def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check(lib.radix_sort_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src)), "copy_probe")
+
+
+class KernelTimer:
+    """Context manager: HIP-event times of every kernel the library enqueues inside it.
+
+    After exit, ``ms`` and ``launches`` hold per-kind sums for the kinds
+    "clear", "histogram", "sweep", "copy".
+    """
+    KINDS = ("clear", "histogram", "sweep", "copy")
+
+    def __enter__(self):
+        _check(load_library().radix_sort_timing_begin(), "timing_begin")
+        return self
+
+    def __exit__(self, *exc):
+        ms = (ctypes.c_double * 4)()
+        nl = (ctypes.c_int * 4)()
+        _check(load_library().radix_sort_timing_end(ms, nl), "timing_end")
+        self.ms = dict(zip(self.KINDS, list(ms)))
+        self.launches = dict(zip(self.KINDS, list(nl)))
+        return False

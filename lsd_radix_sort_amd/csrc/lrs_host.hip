@@ -1,0 +1,509 @@
+// lrs_host.hip -- host driver and C ABI of the LSD radix sort (gfx950).
+//
+// A sort is: one clear of the workspace counters, one all-pass digit
+// histogram, then one sweep launch per digit pass, low digit first, each
+// reading the previous pass's output (CUDA Handbook ch.16: the driver runs one
+// pass per digit, ping-ponging two buffers; here the caller's output is one of
+// the two and the rotation is chosen so the last pass lands in it, so the
+// input is never written).  Everything is enqueued on the caller's stream; the
+// library allocates nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/lsd_radix_sort.h"
+#include "lrs_kernels.h"
+
+namespace lrs {
+namespace {
+
+constexpr int kItems = 16;                       // keys per thread in a sweep tile
+constexpr uint32_t kTile = kBlock * kItems;      // keys per sweep tile
+constexpr uint64_t kAlign = 256;
+constexpr uint32_t kHistTargetBlocks = 2048;
+constexpr uint32_t kHistMinChunk = 4096;
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+bool digit_bits_ok(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+
+// ---------------------------------------------------------------- timing
+
+struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> pool;  // pairs: start, stop
+    std::vector<int> kind;
+    size_t used = 0;
+};
+Timing g_timing;
+constexpr size_t kMaxTimed = 65536;
+
+// Brackets one launch with events when timing is on.  Returns the pair index or -1.
+struct TimedLaunch {
+    int idx = -1;
+    hipStream_t s;
+    TimedLaunch(int kind, hipStream_t stream) : s(stream) {
+        if (!g_timing.on || g_timing.used >= kMaxTimed) return;
+        const size_t i = g_timing.used;
+        if (g_timing.pool.size() < 2 * (i + 1)) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess) return;
+            if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+            g_timing.pool.push_back(a);
+            g_timing.pool.push_back(b);
+        }
+        if (hipEventRecord(g_timing.pool[2 * i], s) != hipSuccess) return;
+        g_timing.kind.resize(i + 1);
+        g_timing.kind[i] = kind;
+        g_timing.used = i + 1;
+        idx = static_cast<int>(i);
+    }
+    void done() {
+        if (idx >= 0) (void)hipEventRecord(g_timing.pool[2 * idx + 1], s);
+    }
+};
+
+// ------------------------------------------------------------ planning
+
+struct Plan {
+    uint64_t rows = 1;
+    uint64_t row_len = 0;
+    int passes = 0;
+    int b = 8;
+    int begin_bit = 0;
+    int end_bit = 32;
+    uint32_t tiles_per_row = 0;
+    uint64_t num_tiles = 0;
+    bool wide_status = false;       // 64-bit look-back words (row_len >= 2^30)
+    uint32_t hist_chunk = 0;
+    uint32_t hist_chunks_per_row = 0;
+    // workspace layout (byte offsets)
+    uint64_t off_hist = 0, hist_words = 0;
+    uint64_t off_counters = 0, counter_words = 0;
+    uint64_t off_status[2] = {0, 0}, status_bytes = 0;
+    uint64_t off_alt_keys = 0, off_alt_vals = 0, off_idx[2] = {0, 0};
+    uint64_t total = 0;
+};
+
+// kind: 0 keys, 1 pairs, 2 segmented
+Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int b, int kind) {
+    Plan p;
+    p.rows = rows;
+    p.row_len = row_len;
+    p.b = b;
+    p.begin_bit = begin_bit;
+    p.end_bit = end_bit;
+    p.passes = static_cast<int>(cdiv(static_cast<uint64_t>(end_bit - begin_bit), b));
+    const uint64_t R = 1ull << b;
+    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, kTile));
+    p.num_tiles = rows * p.tiles_per_row;
+    p.wide_status = row_len >= (1ull << 30);
+
+    // histogram chunking: about kHistTargetBlocks workgroups in all
+    uint64_t chunks = std::max<uint64_t>(1, std::min<uint64_t>(cdiv(row_len, kHistMinChunk),
+                                                                cdiv(kHistTargetBlocks, rows)));
+    uint64_t chunk = align_up(cdiv(row_len, chunks), 1024);
+    p.hist_chunk = static_cast<uint32_t>(std::min<uint64_t>(chunk, 0x80000000ull));
+    p.hist_chunks_per_row = static_cast<uint32_t>(cdiv(row_len, p.hist_chunk));
+
+    const uint64_t keysz = (kind == 2) ? 2 : 4;
+    const uint64_t n = rows * row_len;
+    uint64_t off = 0;
+    p.off_hist = off;
+    p.hist_words = rows * p.passes * R;
+    off = align_up(off + 4 * p.hist_words, kAlign);
+    p.off_counters = off;
+    p.counter_words = static_cast<uint64_t>(p.passes);
+    off = align_up(off + 4 * p.counter_words, kAlign);
+    p.status_bytes = p.num_tiles * R * (p.wide_status ? 8 : 4);
+    const int status_bufs = p.passes > 1 ? 2 : 1;
+    for (int i = 0; i < status_bufs; ++i) {
+        p.off_status[i] = off;
+        off = align_up(off + p.status_bytes, kAlign);
+    }
+    if (p.passes > 1) {
+        p.off_alt_keys = off;
+        off = align_up(off + n * keysz, kAlign);
+        if (kind == 1) {
+            p.off_alt_vals = off;
+            off = align_up(off + n * 4, kAlign);
+        }
+        if (kind == 2) {
+            p.off_idx[0] = off;
+            off = align_up(off + n * 4, kAlign);
+            if (p.passes > 2) {
+                p.off_idx[1] = off;
+                off = align_up(off + n * 4, kAlign);
+            }
+        }
+    }
+    p.total = off;
+    return p;
+}
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// ------------------------------------------------------------ launches
+
+template <int B, int KK>
+hipError_t launch_hist_b(const HistArgs &a, uint32_t blocks, hipStream_t s) {
+    histogram_kernel<B, KK><<<blocks, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int KK>
+hipError_t launch_hist(int b, const HistArgs &a, uint32_t blocks, hipStream_t s) {
+    switch (b) {
+        case 1: return launch_hist_b<1, KK>(a, blocks, s);
+        case 2: return launch_hist_b<2, KK>(a, blocks, s);
+        case 4: return launch_hist_b<4, KK>(a, blocks, s);
+        default: return launch_hist_b<8, KK>(a, blocks, s);
+    }
+}
+
+// Digit-group matching used by the sweep: LDS masks by default; the
+// environment variable LRS_MATCH=ballot selects the ballot form (both are
+// complete implementations; the switch exists to compare them).
+int match_kind() {
+    static const int kind = [] {
+        const char *e = std::getenv("LRS_MATCH");
+        return (e != nullptr && std::strcmp(e, "ballot") == 0) ? int(kMatchBallot) : int(kMatchLds);
+    }();
+    return kind;
+}
+
+template <int B, int KK, int PK>
+hipError_t launch_sweep_b(const SweepArgs &a, bool wide, uint64_t tiles, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(tiles));
+    if (match_kind() == kMatchBallot) {
+        if (wide) sweep_kernel<B, kItems, KK, PK, uint64_t, kMatchBallot><<<grid, kBlock, 0, s>>>(a);
+        else sweep_kernel<B, kItems, KK, PK, uint32_t, kMatchBallot><<<grid, kBlock, 0, s>>>(a);
+    } else {
+        if (wide) sweep_kernel<B, kItems, KK, PK, uint64_t, kMatchLds><<<grid, kBlock, 0, s>>>(a);
+        else sweep_kernel<B, kItems, KK, PK, uint32_t, kMatchLds><<<grid, kBlock, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int KK, int PK>
+hipError_t launch_sweep(int b, const SweepArgs &a, bool wide, uint64_t tiles, hipStream_t s) {
+    switch (b) {
+        case 1: return launch_sweep_b<1, KK, PK>(a, wide, tiles, s);
+        case 2: return launch_sweep_b<2, KK, PK>(a, wide, tiles, s);
+        case 4: return launch_sweep_b<4, KK, PK>(a, wide, tiles, s);
+        default: return launch_sweep_b<8, KK, PK>(a, wide, tiles, s);
+    }
+}
+
+hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, hipStream_t s) {
+    ClearArgs c{};
+    c.p[0] = need_hist ? reinterpret_cast<uint32_t *>(ws + p.off_hist) : nullptr;
+    c.words[0] = p.hist_words;
+    c.p[1] = reinterpret_cast<uint32_t *>(ws + p.off_counters);
+    c.words[1] = p.counter_words;
+    c.p[2] = reinterpret_cast<uint32_t *>(ws + p.off_status[0]);
+    c.words[2] = p.status_bytes / 4;
+    const uint64_t words = std::max<uint64_t>(c.words[0] * need_hist, c.words[2]);
+    const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(2048, std::max<uint64_t>(1, cdiv(words / 4, kBlock))));
+    TimedLaunch t(0, s);
+    clear_kernel<<<blocks, kBlock, 0, s>>>(c);
+    hipError_t e = hipGetLastError();
+    t.done();
+    return e;
+}
+
+hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint32_t flip,
+                            bool accumulate, hipStream_t s) {
+    HistArgs h{};
+    h.keys = keys;
+    h.hist = hist;
+    h.row_len = static_cast<uint32_t>(p.row_len);
+    h.chunks_per_row = p.hist_chunks_per_row;
+    h.chunk = p.hist_chunk;
+    h.passes = static_cast<uint32_t>(p.passes);
+    h.begin_bit = static_cast<uint32_t>(p.begin_bit);
+    h.end_bit = static_cast<uint32_t>(p.end_bit);
+    h.flip = flip;
+    h.atomic = accumulate ? 1u : 0u;
+    const uint64_t blocks = p.rows * p.hist_chunks_per_row;
+    TimedLaunch t(1, s);
+    hipError_t e = (kk == kKeyU32) ? launch_hist<kKeyU32>(p.b, h, static_cast<uint32_t>(blocks), s)
+                                   : launch_hist<kKeyF16>(p.b, h, static_cast<uint32_t>(blocks), s);
+    t.done();
+    return e;
+}
+
+SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass) {
+    SweepArgs a{};
+    const uint64_t R = 1ull << p.b;
+    a.hist = reinterpret_cast<const uint32_t *>(ws + p.off_hist) + static_cast<uint64_t>(pass) * R;
+    a.hist_row_stride = static_cast<uint32_t>(p.passes * R);
+    a.status = ws + p.off_status[pass & 1];
+    a.status_next = (pass + 1 < p.passes) ? ws + p.off_status[(pass + 1) & 1] : nullptr;
+    a.tile_counter = reinterpret_cast<uint32_t *>(ws + p.off_counters) + pass;
+    a.row_len = static_cast<uint32_t>(p.row_len);
+    a.tiles_per_row = p.tiles_per_row;
+    a.num_tiles = static_cast<uint32_t>(p.num_tiles);
+    const int shift = p.begin_bit + pass * p.b;
+    const int width = std::min(p.b, p.end_bit - shift);
+    a.shift = static_cast<uint32_t>(shift);
+    a.digit_mask = (1u << width) - 1u;
+    a.flip = 0;
+    return a;
+}
+
+// Buffer that pass `pass` writes: the last pass writes the caller's output,
+// earlier passes alternate backwards between the spare buffer and the output.
+template <typename T>
+T *pass_dst(int pass, int passes, T *out, T *alt) {
+    return ((passes - 1 - pass) % 2 == 0) ? out : alt;
+}
+
+int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+             uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int b, void *workspace,
+             size_t ws_bytes, void *stream) {
+    if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
+    if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
+    if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
+    if (n == 0) return LRS_OK;
+    if (!keys_in || !keys_out || (pairs && (!vals_in || !vals_out)) || !workspace)
+        return LRS_ERR_NULL_POINTER;
+    if (misaligned(keys_in, 4) || misaligned(keys_out, 4) || misaligned(workspace, 256) ||
+        (pairs && (misaligned(vals_in, 4) || misaligned(vals_out, 4))))
+        return LRS_ERR_ALIGNMENT;
+    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0);
+    if (ws_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
+    const uint64_t kb = 4 * n;
+    if (overlaps(keys_out, kb, keys_in, kb) || overlaps(keys_out, kb, workspace, p.total) ||
+        (pairs && (overlaps(vals_out, kb, vals_in, kb) || overlaps(vals_out, kb, keys_in, kb) ||
+                   overlaps(keys_out, kb, vals_in, kb) || overlaps(vals_out, kb, keys_out, kb) ||
+                   overlaps(vals_out, kb, workspace, p.total))))
+        return LRS_ERR_ALIASING;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, keys_in, hist, kKeyU32, 0, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+
+    uint32_t *alt_k = reinterpret_cast<uint32_t *>(ws + p.off_alt_keys);
+    uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
+    const uint32_t *src_k = keys_in;
+    const uint32_t *src_v = vals_in;
+    for (int pass = 0; pass < p.passes; ++pass) {
+        SweepArgs a = pass_args(p, ws, pass);
+        uint32_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
+        a.keys_in = src_k;
+        a.keys_out = dk;
+        hipError_t e;
+        TimedLaunch t(2, s);
+        if (pairs) {
+            uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
+            a.vals_in = src_v;
+            a.vals_out = dv;
+            e = launch_sweep<kKeyU32, kPayU32>(b, a, p.wide_status, p.num_tiles, s);
+            src_v = dv;
+        } else {
+            e = launch_sweep<kKeyU32, kPayNone>(b, a, p.wide_status, p.num_tiles, s);
+        }
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+        src_k = dk;
+    }
+    return LRS_OK;
+}
+
+}  // namespace
+}  // namespace lrs
+
+using namespace lrs;
+
+extern "C" {
+
+size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int digit_bits,
+                                 int with_values) {
+    if (!digit_bits_ok(digit_bits) || begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit ||
+        n == 0 || n > LRS_MAX_KEYS)
+        return 0;
+    return static_cast<size_t>(make_plan(1, n, begin_bit, end_bit, digit_bits, with_values ? 1 : 0).total);
+}
+
+int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int begin_bit,
+                    int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return sort_u32(false, keys_in, nullptr, keys_out, nullptr, n, begin_bit, end_bit, digit_bits,
+                    workspace, workspace_bytes, stream);
+}
+
+int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+                     uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    return sort_u32(true, keys_in, vals_in, keys_out, vals_out, n, begin_bit, end_bit, digit_bits,
+                    workspace, workspace_bytes, stream);
+}
+
+size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits) {
+    if (!digit_bits_ok(digit_bits) || rows <= 0 || n <= 0 ||
+        static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
+        static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40))
+        return 0;
+    return static_cast<size_t>(make_plan(rows, n, 0, 16, digit_bits, 2).total);
+}
+
+int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx_out,
+                       int64_t rows, int64_t n, int dtype, int descending, int digit_bits,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
+    if (dtype != LRS_DTYPE_FP16 && dtype != LRS_DTYPE_BF16) return LRS_ERR_DTYPE;
+    if (rows < 0 || n < 0 || static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
+        (rows > 0 && static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40)))
+        return LRS_ERR_SIZE;
+    if (rows == 0 || n == 0) return LRS_OK;
+    if (!vals_in || !vals_out || !idx_out || !workspace) return LRS_ERR_NULL_POINTER;
+    if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(idx_out, 8) ||
+        misaligned(workspace, 256))
+        return LRS_ERR_ALIGNMENT;
+    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2);
+    if (p.num_tiles > 0x7FFFFFFFull || p.rows * p.hist_chunks_per_row > 0x7FFFFFFFull) return LRS_ERR_SIZE;
+    if (workspace_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
+    const uint64_t cnt = static_cast<uint64_t>(rows) * n;
+    if (overlaps(vals_out, 2 * cnt, vals_in, 2 * cnt) || overlaps(idx_out, 8 * cnt, vals_in, 2 * cnt) ||
+        overlaps(idx_out, 8 * cnt, vals_out, 2 * cnt) || overlaps(vals_out, 2 * cnt, workspace, p.total) ||
+        overlaps(idx_out, 8 * cnt, workspace, p.total))
+        return LRS_ERR_ALIASING;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const uint32_t flip = descending ? 0xFFFFu : 0u;
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+
+    uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
+    uint32_t *idx[2] = {reinterpret_cast<uint32_t *>(ws + p.off_idx[0]),
+                        reinterpret_cast<uint32_t *>(ws + p.off_idx[1])};
+    const uint16_t *src_k = vals_in;
+    for (int pass = 0; pass < p.passes; ++pass) {
+        SweepArgs a = pass_args(p, ws, pass);
+        a.flip = flip;
+        uint16_t *dk = pass_dst(pass, p.passes, vals_out, alt_k);
+        a.keys_in = src_k;
+        a.keys_out = dk;
+        hipError_t e;
+        TimedLaunch t(2, s);
+        if (pass == 0) {
+            a.vals_in = nullptr;
+            a.vals_out = idx[0];
+            e = launch_sweep<kKeyF16, kPayIdxFirst>(digit_bits, a, false, p.num_tiles, s);
+        } else if (pass + 1 < p.passes) {
+            a.vals_in = idx[(pass - 1) & 1];
+            a.vals_out = idx[pass & 1];
+            e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, false, p.num_tiles, s);
+        } else {
+            a.vals_in = idx[(pass - 1) & 1];
+            a.vals_out = idx_out;
+            e = launch_sweep<kKeyF16, kPayIdxLast>(digit_bits, a, false, p.num_tiles, s);
+        }
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+        src_k = dk;
+    }
+    return LRS_OK;
+}
+
+int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit,
+                                int digit_bits, uint32_t *hist_out, void *stream) {
+    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
+    if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
+    if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
+    if (!hist_out || (n && !keys)) return LRS_ERR_NULL_POINTER;
+    if (misaligned(keys, 4) || misaligned(hist_out, 16)) return LRS_ERR_ALIGNMENT;
+    const Plan p = make_plan(1, n ? n : 1, begin_bit, end_bit, digit_bits, 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ClearArgs c{};
+    c.p[0] = hist_out;
+    c.words[0] = p.hist_words;
+    {
+        TimedLaunch t(0, s);
+        clear_kernel<<<1, kBlock, 0, s>>>(c);
+        hipError_t e = hipGetLastError();
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+    }
+    if (n == 0) return LRS_OK;
+    return launch_histogram(p, keys, hist_out, kKeyU32, 0, true, s) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
+int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return LRS_OK;
+    if (!src || !dst) return LRS_ERR_NULL_POINTER;
+    if (misaligned(src, 16) || misaligned(dst, 16)) return LRS_ERR_ALIGNMENT;
+    if (overlaps(src, bytes, dst, bytes)) return LRS_ERR_ALIASING;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint64_t n16 = bytes / 16;
+    const uint32_t tail = static_cast<uint32_t>(bytes % 16);
+    const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(8192, std::max<uint64_t>(1, cdiv(n16, kBlock * 4))));
+    TimedLaunch t(3, s);
+    copy_kernel<<<blocks, kBlock, 0, s>>>(static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16,
+                                          static_cast<const uint8_t *>(src) + n16 * 16,
+                                          static_cast<uint8_t *>(dst) + n16 * 16, tail);
+    hipError_t e = hipGetLastError();
+    t.done();
+    return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
+int radix_sort_timing_begin(void) {
+    g_timing.on = true;
+    g_timing.used = 0;
+    g_timing.kind.clear();
+    return LRS_OK;
+}
+
+int radix_sort_timing_end(double *ms_by_kind, int *launches_by_kind) {
+    for (int k = 0; k < 4; ++k) {
+        if (ms_by_kind) ms_by_kind[k] = 0.0;
+        if (launches_by_kind) launches_by_kind[k] = 0;
+    }
+    g_timing.on = false;
+    for (size_t i = 0; i < g_timing.used; ++i) {
+        if (hipEventSynchronize(g_timing.pool[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_timing.pool[2 * i], g_timing.pool[2 * i + 1]) != hipSuccess)
+            return LRS_ERR_HIP;
+        const int k = g_timing.kind[i];
+        if (ms_by_kind) ms_by_kind[k] += ms;
+        if (launches_by_kind) launches_by_kind[k] += 1;
+    }
+    g_timing.used = 0;
+    return LRS_OK;
+}
+
+const char *radix_sort_status_string(int status) {
+    switch (status) {
+        case LRS_OK: return "ok";
+        case LRS_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case LRS_ERR_BIT_RANGE: return "bit window must satisfy 0 <= begin_bit < end_bit <= key width";
+        case LRS_ERR_DIGIT_BITS: return "digit_bits must be 1, 2, 4 or 8";
+        case LRS_ERR_SIZE: return "element count or shape beyond the supported limit";
+        case LRS_ERR_ALIASING: return "an output overlaps an input, another output or the workspace";
+        case LRS_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_size() figure";
+        case LRS_ERR_DTYPE: return "dtype must be LRS_DTYPE_FP16 or LRS_DTYPE_BF16";
+        case LRS_ERR_HIP: return "the HIP runtime rejected a launch";
+        case LRS_ERR_ALIGNMENT: return "a pointer is not aligned as required";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

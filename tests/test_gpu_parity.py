@@ -1,0 +1,271 @@
+"""GPU parity: the HIP library against the CPU oracle, element for element,
+tolerance 0 (keys, payloads and indices), on the seeded inputs of the five
+workloads and on edge cases.  At the 2^28-pair size the result is checked by
+the properties that characterise the unique stable sort (sorted, a permutation
+carried by the index payload, ties in input order) computed on the GPU with
+torch, plus oracle positions of sampled elements computed one by one."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import window
+
+pytestmark = pytest.mark.gpu
+
+lrs = pytest.importorskip("lsd_radix_sort_amd")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lrs.load_library()
+    return torch.device("cuda:0")
+
+
+def to_gpu(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32).copy()).cuda()
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).cuda()
+    return torch.from_numpy(a.copy()).cuda()
+
+
+def to_np_u32(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def gpu_keys(keys, begin, end, b):
+    kt = to_gpu(keys)
+    out = lrs.radix_sort_keys(kt, begin, end, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np_u32(kt), keys), "input was written"
+    return to_np_u32(out)
+
+
+def gpu_pairs(keys, vals, begin, end, b):
+    kt, vt = to_gpu(keys), to_gpu(vals)
+    ko, vo = lrs.radix_sort_pairs(kt, vt, begin, end, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np_u32(kt), keys) and np.array_equal(to_np_u32(vt), vals), "input was written"
+    return to_np_u32(ko), to_np_u32(vo)
+
+
+def assert_same(got, exp, what):
+    if not np.array_equal(got, exp):
+        bad = np.nonzero(got != exp)[0]
+        raise AssertionError(f"{what}: {bad.size} mismatches, first at {bad[0]}: got {got[bad[0]]}, "
+                             f"expected {exp[bad[0]]}")
+
+
+# ----------------------------------------------------------------- u32 keys
+
+@pytest.mark.parametrize("b", [4, 1, 2, 8])
+def test_c1_1024_keys_12_bits(b):
+    keys = workloads.keys_c1()
+    log(f"c1 b={b}")
+    exp = oracle.radix_sort_keys(keys, 0, 12, b)
+    assert_same(gpu_keys(keys, 0, 12, b), exp, f"c1 b={b}")
+
+
+@pytest.mark.parametrize("b", [4, 8])
+def test_c2_4m_keys(b):
+    keys = workloads.keys_c2()
+    log(f"c2 b={b}")
+    exp = oracle.radix_sort_keys(keys, 0, 32, b)
+    assert_same(exp, np.sort(keys), "oracle vs np.sort")
+    assert_same(gpu_keys(keys, 0, 32, b), exp, f"c2 b={b}")
+
+
+@pytest.mark.parametrize("dist", ["uniform", "and3"])
+def test_c3_pairs_reduced_size(dist):
+    n = 1 << 22
+    keys, vals = workloads.pairs_c3(n, dist)
+    log(f"c3 reduced n={n} {dist}")
+    ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
+    gk, gv = gpu_pairs(keys, vals, 0, 32, 8)
+    assert_same(gk, ek, "keys")
+    assert_same(gv, ev, "values")
+
+
+def test_pass_by_pass_states():
+    # the state after p passes is the stable sort by the low p*b bits of the window
+    n = 300_001
+    keys = workloads.random_u32(31, n) & workloads.random_u32(32, n)
+    vals = np.arange(n, dtype=np.uint32)
+    for b, begin in ((8, 0), (4, 3), (1, 20), (2, 5)):
+        P = oracle.num_passes(begin, 32, b)
+        for p in range(1, P + 1):
+            end = min(32, begin + p * b)
+            ek, ev = oracle.radix_sort_pairs(keys, vals, begin, end, b)
+            gk, gv = gpu_pairs(keys, vals, begin, end, b)
+            assert_same(gk, ek, f"b={b} begin={begin} passes={p} keys")
+            assert_same(gv, ev, f"b={b} begin={begin} passes={p} values")
+
+
+def test_fuzz_sizes_windows_widths():
+    rng = np.random.default_rng(2024)
+    sizes = [1, 2, 63, 64, 65, 255, 4095, 4096, 4097, 8191, 8193, 12289, 65537, 100_003]
+    for trial, n in enumerate(sizes + [int(x) for x in rng.integers(1, 200_000, 10)]):
+        keys = workloads.random_u32(700 + trial, n)
+        if trial % 2:
+            keys &= workloads.random_u32(900 + trial, n)
+        begin = int(rng.integers(0, 31))
+        end = int(rng.integers(begin + 1, 33))
+        b = int(rng.choice([1, 2, 4, 8]))
+        vals = workloads.random_u32(1100 + trial, n)
+        ek, ev = oracle.radix_sort_pairs(keys, vals, begin, end, b)
+        gk, gv = gpu_pairs(keys, vals, begin, end, b)
+        assert_same(gk, ek, f"n={n} [{begin},{end}) b={b} keys")
+        assert_same(gv, ev, f"n={n} [{begin},{end}) b={b} values")
+        assert_same(gpu_keys(keys, begin, end, b), ek, f"n={n} keys-only")
+
+
+def test_degenerate_inputs():
+    n = 50_000
+    cases = {
+        "all_equal": np.full(n, 0xDEADBEEF, dtype=np.uint32),
+        "all_max": np.full(n, 0xFFFFFFFF, dtype=np.uint32),
+        "all_zero": np.zeros(n, dtype=np.uint32),
+        "sorted": np.arange(n, dtype=np.uint32) * np.uint32(977),
+        "reversed": (np.arange(n, dtype=np.uint32) * np.uint32(977))[::-1].copy(),
+        "two_values": np.where(workloads.random_u32(5, n) & 1, 0xFFFFFFFF, 0).astype(np.uint32),
+    }
+    vals = np.arange(n, dtype=np.uint32)
+    for name, keys in cases.items():
+        for b in (1, 8):
+            ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, b)
+            gk, gv = gpu_pairs(keys, vals, 0, 32, b)
+            assert_same(gk, ek, f"{name} b={b}")
+            assert_same(gv, ev, f"{name} b={b} values")
+
+
+def test_empty_input():
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    assert lrs.radix_sort_keys(e).numel() == 0
+    k, v = lrs.radix_sort_pairs(e, e.clone())
+    assert k.numel() == 0 and v.numel() == 0
+    x = torch.empty(0, 16, dtype=torch.float16, device="cuda")
+    vs, ix = lrs.segmented_row_sort(x)
+    assert vs.shape == (0, 16) and ix.shape == (0, 16)
+
+
+def test_digit_histograms():
+    keys = workloads.pairs_c3(1 << 20, "and3")[0]
+    kt = to_gpu(keys)
+    for begin, end, b in ((0, 32, 8), (0, 32, 4), (0, 12, 4), (3, 30, 1), (5, 17, 2)):
+        h = lrs.radix_sort_digit_histograms(kt, begin, end, b)
+        torch.cuda.synchronize()
+        exp = oracle.all_pass_histograms(keys, begin, end, b)
+        assert np.array_equal(h.cpu().numpy().astype(np.uint64), exp), (begin, end, b)
+
+
+def test_validation_with_real_buffers():
+    n = 4096
+    k = torch.zeros(n, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(k)
+    with pytest.raises(ValueError):
+        lrs.radix_sort_keys(k, 0, 32, 3)
+    with pytest.raises(ValueError):
+        lrs.radix_sort_keys(k, 0, 33, 8)
+    with pytest.raises(ValueError):
+        lrs.radix_sort_keys(k, out=k)
+    ws = torch.empty(lrs.radix_sort_workspace_size(n, 0, 32, 8), dtype=torch.uint8, device="cuda")
+    lib = lrs.load_library()
+    st = lib.radix_sort_keys(k.data_ptr(), o.data_ptr(), n, 0, 32, 8, ws.data_ptr(), ws.numel() - 1, None)
+    assert st == 6
+    x = torch.zeros(4, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        lrs.segmented_row_sort(x, digit_bits=5)
+
+
+# -------------------------------------------------------------- full size
+
+def _u32_to_i64(t):
+    return t.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+
+
+@pytest.mark.parametrize("dist", ["uniform", "and3"])
+def test_c3_full_size_properties_and_samples(dist):
+    n = 1 << 28
+    log(f"c3 full n={n} {dist}: generating")
+    keys, vals = workloads.pairs_c3(n, dist)
+    kt, vt = to_gpu(keys), to_gpu(vals)
+    log("c3 full: sorting")
+    ko, vo = lrs.radix_sort_pairs(kt, vt, 0, 32, 8)
+    torch.cuda.synchronize()
+    log("c3 full: checking properties")
+    k64 = _u32_to_i64(ko)
+    idx = _u32_to_i64(vo)
+    assert bool((k64[1:] >= k64[:-1]).all()), "not sorted"
+    seen = torch.zeros(n, dtype=torch.bool, device="cuda")
+    seen[idx] = True
+    assert bool(seen.all()), "values are not a permutation"
+    del seen
+    assert bool((_u32_to_i64(kt)[idx] == k64).all()), "key/value mismatch"
+    ties = k64[1:] == k64[:-1]
+    assert bool(((idx[1:] > idx[:-1]) | ~ties).all()), "unstable"
+    del ties, k64
+    log("c3 full: sampled oracle positions")
+    gk, gv = to_np_u32(ko), to_np_u32(vo)
+    rng = np.random.default_rng(7)
+    for i in [0, n - 1] + [int(x) for x in rng.integers(0, n, 6)]:
+        pos = oracle.stable_position(keys, 0, 32, i)
+        assert gk[pos] == keys[i] and gv[pos] == vals[i], (i, pos)
+    assert np.array_equal(to_np_u32(kt), keys), "input was written"
+
+
+# -------------------------------------------------------------- segmented
+
+def gpu_rows(bits: np.ndarray, dtype: str, descending: bool, b: int):
+    t = to_gpu(bits).view(torch.float16 if dtype == "fp16" else torch.bfloat16)
+    vo, io = lrs.segmented_row_sort(t, descending, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.view(torch.int16).cpu().numpy().view(np.uint16), bits), "input was written"
+    return vo.view(torch.int16).cpu().numpy().view(np.uint16), io.cpu().numpy()
+
+
+def test_c4_fp16_1024x65536_ascending():
+    bits = workloads.matrix_c4()
+    log("c4 oracle")
+    ev, ei = oracle.segmented_row_sort(bits, False, 4)
+    log("c4 gpu")
+    gv, gi = gpu_rows(bits, "fp16", False, 4)
+    assert_same(gv.ravel(), ev.ravel(), "c4 values")
+    assert_same(gi.ravel(), ei.ravel(), "c4 indices")
+
+
+def test_c5_bf16_4096x4096_descending():
+    bits = workloads.matrix_c5()
+    log("c5 oracle")
+    ev, ei = oracle.segmented_row_sort(bits, True, 8)
+    log("c5 gpu")
+    gv, gi = gpu_rows(bits, "bf16", True, 8)
+    assert_same(gv.ravel(), ev.ravel(), "c5 values")
+    assert_same(gi.ravel(), ei.ravel(), "c5 indices")
+
+
+@pytest.mark.parametrize("rows,n", [(1, 1), (3, 7), (5, 4095), (2, 4097), (7, 12345), (1, 70000),
+                                     (300, 33), (2, 200_000)])
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+def test_rows_ragged_shapes(rows, n, b):
+    bits = workloads.fp16_normal_bits(rows * 131 + n, rows * n).reshape(rows, n)
+    bits[:, ::17] = np.uint16(0x8000)  # -0
+    bits[:, 5::19] = np.uint16(0x0000)  # +0
+    bits[:, 3::23] = np.uint16(0x7E00)  # NaN
+    bits[:, 7::29] = np.uint16(0xFC00)  # -inf
+    for desc in (False, True):
+        ev, ei = oracle.segmented_row_sort(bits, desc, b)
+        for dtype in ("fp16", "bf16"):
+            gv, gi = gpu_rows(bits, dtype, desc, b)
+            assert_same(gv.ravel(), ev.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype}")
+            assert_same(gi.ravel(), ei.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype} idx")
