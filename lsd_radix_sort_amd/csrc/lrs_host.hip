@@ -22,8 +22,27 @@
 namespace lrs {
 namespace {
 
-constexpr int kItems = 16;                       // keys per thread in a sweep tile
-constexpr uint32_t kTile = kBlock * kItems;      // keys per sweep tile
+// Sweep tile shapes (threads x keys per thread).  Long rows use the largest;
+// shorter inputs a smaller one so the grid still has several tiles per CU and
+// little of the last tile of each row is padding.
+struct TileCfg {
+    int block;
+    int items;
+    uint64_t tile;
+};
+constexpr TileCfg kTileCfgs[3] = {
+    {256, 16, 4096}, {512, 16, 8192}, {kSweepBlock, LRS_SWEEP_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_ITEMS}};
+constexpr uint64_t kMinTiles = 1024;  // about four tiles per CU
+
+int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
+    for (int c = 2; c >= 1; --c) {
+        const uint64_t tile = kTileCfgs[c].tile;
+        const uint64_t tiles = rows * ((row_len + tile - 1) / tile);
+        const uint64_t padded = tiles * tile;
+        if (tiles >= kMinTiles && (padded - rows * row_len) * 10 <= padded) return c;
+    }
+    return 0;
+}
 constexpr uint64_t kAlign = 256;
 constexpr uint32_t kHistTargetBlocks = 2048;
 constexpr uint32_t kHistMinChunk = 4096;
@@ -78,9 +97,10 @@ struct Plan {
     int b = 8;
     int begin_bit = 0;
     int end_bit = 32;
+    int tile_cfg = 0;
     uint32_t tiles_per_row = 0;
     uint64_t num_tiles = 0;
-    bool wide_status = false;       // 64-bit look-back words (row_len >= 2^30)
+    bool wide_status = false;       // 64-bit look-back words, 64-bit stores (row_len >= 2^29)
     uint32_t hist_chunk = 0;
     uint32_t hist_chunks_per_row = 0;
     // workspace layout (byte offsets)
@@ -101,9 +121,10 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.end_bit = end_bit;
     p.passes = static_cast<int>(cdiv(static_cast<uint64_t>(end_bit - begin_bit), b));
     const uint64_t R = 1ull << b;
-    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, kTile));
+    p.tile_cfg = choose_tile_cfg(rows, row_len);
+    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, kTileCfgs[p.tile_cfg].tile));
     p.num_tiles = rows * p.tiles_per_row;
-    p.wide_status = row_len >= (1ull << 30);
+    p.wide_status = row_len >= (1ull << 29);
 
     // histogram chunking: about kHistTargetBlocks workgroups in all
     uint64_t chunks = std::max<uint64_t>(1, std::min<uint64_t>(cdiv(row_len, kHistMinChunk),
@@ -173,37 +194,53 @@ hipError_t launch_hist(int b, const HistArgs &a, uint32_t blocks, hipStream_t s)
     }
 }
 
-// Digit-group matching used by the sweep: LDS masks by default; the
-// environment variable LRS_MATCH=ballot selects the ballot form (both are
-// complete implementations; the switch exists to compare them).
+// Digit-group matching used by the sweep: LRS_MATCH_DEFAULT unless the
+// environment variable LRS_MATCH is "ballot" or "lds" (both are complete
+// implementations; the switch exists to compare them).
+#ifndef LRS_MATCH_DEFAULT
+#define LRS_MATCH_DEFAULT 0  // kMatchBallot
+#endif
 int match_kind() {
     static const int kind = [] {
         const char *e = std::getenv("LRS_MATCH");
-        return (e != nullptr && std::strcmp(e, "ballot") == 0) ? int(kMatchBallot) : int(kMatchLds);
+        if (e != nullptr && std::strcmp(e, "ballot") == 0) return int(kMatchBallot);
+        if (e != nullptr && std::strcmp(e, "lds") == 0) return int(kMatchLds);
+        return int(LRS_MATCH_DEFAULT);
     }();
     return kind;
 }
 
-template <int B, int KK, int PK>
-hipError_t launch_sweep_b(const SweepArgs &a, bool wide, uint64_t tiles, hipStream_t s) {
+template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W>
+void launch_sweep_cfg(const SweepArgs &a, uint64_t tiles, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(tiles));
-    if (match_kind() == kMatchBallot) {
-        if (wide) sweep_kernel<B, kItems, KK, PK, uint64_t, kMatchBallot><<<grid, kBlock, 0, s>>>(a);
-        else sweep_kernel<B, kItems, KK, PK, uint32_t, kMatchBallot><<<grid, kBlock, 0, s>>>(a);
-    } else {
-        if (wide) sweep_kernel<B, kItems, KK, PK, uint64_t, kMatchLds><<<grid, kBlock, 0, s>>>(a);
-        else sweep_kernel<B, kItems, KK, PK, uint32_t, kMatchLds><<<grid, kBlock, 0, s>>>(a);
-    }
+    if (match_kind() == kMatchBallot)
+        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchBallot><<<grid, BLOCK, 0, s>>>(a);
+    else
+        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchLds><<<grid, BLOCK, 0, s>>>(a);
+}
+
+template <int B, int KK, int PK>
+hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t tiles, hipStream_t s) {
+    // 64-bit look-back words only occur for rows of 2^29 or more elements,
+    // which always take the largest tile.
+    if (wide && KK == kKeyU32)
+        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint64_t>(a, tiles, s);
+    else if (cfg == 2)
+        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint32_t>(a, tiles, s);
+    else if (cfg == 1)
+        launch_sweep_cfg<B, kTileCfgs[1].items, kTileCfgs[1].block, KK, PK, uint32_t>(a, tiles, s);
+    else
+        launch_sweep_cfg<B, kTileCfgs[0].items, kTileCfgs[0].block, KK, PK, uint32_t>(a, tiles, s);
     return hipGetLastError();
 }
 
 template <int KK, int PK>
-hipError_t launch_sweep(int b, const SweepArgs &a, bool wide, uint64_t tiles, hipStream_t s) {
+hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t tiles, hipStream_t s) {
     switch (b) {
-        case 1: return launch_sweep_b<1, KK, PK>(a, wide, tiles, s);
-        case 2: return launch_sweep_b<2, KK, PK>(a, wide, tiles, s);
-        case 4: return launch_sweep_b<4, KK, PK>(a, wide, tiles, s);
-        default: return launch_sweep_b<8, KK, PK>(a, wide, tiles, s);
+        case 1: return launch_sweep_b<1, KK, PK>(a, cfg, wide, tiles, s);
+        case 2: return launch_sweep_b<2, KK, PK>(a, cfg, wide, tiles, s);
+        case 4: return launch_sweep_b<4, KK, PK>(a, cfg, wide, tiles, s);
+        default: return launch_sweep_b<8, KK, PK>(a, cfg, wide, tiles, s);
     }
 }
 
@@ -313,10 +350,10 @@ int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint3
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = launch_sweep<kKeyU32, kPayU32>(b, a, p.wide_status, p.num_tiles, s);
+            e = launch_sweep<kKeyU32, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
             src_v = dv;
         } else {
-            e = launch_sweep<kKeyU32, kPayNone>(b, a, p.wide_status, p.num_tiles, s);
+            e = launch_sweep<kKeyU32, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -406,15 +443,15 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
         if (pass == 0) {
             a.vals_in = nullptr;
             a.vals_out = idx[0];
-            e = launch_sweep<kKeyF16, kPayIdxFirst>(digit_bits, a, false, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayIdxFirst>(digit_bits, a, p.tile_cfg, false, p.num_tiles, s);
         } else if (pass + 1 < p.passes) {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx[pass & 1];
-            e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, false, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, p.tile_cfg, false, p.num_tiles, s);
         } else {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx_out;
-            e = launch_sweep<kKeyF16, kPayIdxLast>(digit_bits, a, false, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayIdxLast>(digit_bits, a, p.tile_cfg, false, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;

@@ -21,11 +21,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lrs {
 
-constexpr int kBlock = 256;            // threads per workgroup
+// Compile-time tunables (defaults are the measured choices).
+#ifndef LRS_SWEEP_ITEMS
+#define LRS_SWEEP_ITEMS 24      // keys per thread in the largest sweep tile
+#endif
+#ifndef LRS_SWEEP_BLOCK
+#define LRS_SWEEP_BLOCK 512     // threads per workgroup of the largest sweep tile
+#endif
+#ifndef LRS_LOOKBACK
+#define LRS_LOOKBACK 4          // predecessor words a look-back lane reads per round trip
+#endif
+#ifndef LRS_HIST_COPIES
+#define LRS_HIST_COPIES 8       // LDS copies of the histogram, lanes spread over them
+#endif
+
+constexpr int kBlock = 256;            // threads per workgroup (histogram, utilities)
+constexpr int kSweepBlock = LRS_SWEEP_BLOCK;
+constexpr int kLookback = LRS_LOOKBACK;
 constexpr int kWave = 64;              // CDNA wavefront width
-constexpr int kWaves = kBlock / kWave;
 
 enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1 };
 
@@ -58,6 +75,44 @@ template <> struct KeyTraits<kKeyF16> {
     }
 };
 
+// Range-checked buffer access: a load past the resource's byte count returns
+// 0 and a store past it is dropped by the hardware, so tile edges need no
+// per-element predicates and a stray index cannot leave its row.
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer resource word 3 (raw, no swizzle)
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename T> struct BufIO;
+template <> struct BufIO<uint32_t> {
+    __device__ static inline uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t i) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(i * 4u), 0, 0);
+    }
+    __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(i * 4u), 0, 0);
+    }
+};
+template <> struct BufIO<uint16_t> {
+    __device__ static inline uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t i) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(i * 2u), 0, 0);
+    }
+    __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(i * 2u), 0, 0);
+    }
+};
+template <> struct BufIO<int64_t> {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
+        const v2u w = {v, 0u};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(i * 8u), 0, 0);
+    }
+};
+
+// Keeps a value materialised in a register at this point (stops the compiler
+// from sinking its computation and keeping the operands alive instead).
+__device__ inline void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
+
 // --------------------------------------------------------- wave utilities
 
 // Lanes of this wave whose digit equals this lane's digit (all 64 lanes must
@@ -88,20 +143,6 @@ __device__ inline uint32_t wave_inclusive_scan(uint32_t x, int lane) {
         if (lane >= o) x += y;
     }
     return x;
-}
-
-// Workgroup-wide exclusive scan of one value per thread.  Every thread of the
-// workgroup must call it.  `tmp` holds kWaves words of LDS.
-__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, int lane, int wave) {
-    const uint32_t inc = wave_inclusive_scan(v, lane);
-    if (lane == kWave - 1) tmp[wave] = inc;
-    __syncthreads();
-    uint32_t before = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-        if (w < wave) before += tmp[w];
-    __syncthreads();
-    return before + inc - v;
 }
 
 // ------------------------------------------------------- look-back status
@@ -149,27 +190,68 @@ struct SweepArgs {
 // How a wave finds the lanes that share its digit.
 enum MatchKind : int { kMatchBallot = 0, kMatchLds = 1 };
 
-template <int B, int ITEMS, int KK, int PK, typename W, int MATCH>
-__global__ __launch_bounds__(kBlock) void sweep_kernel(SweepArgs a) {
+// Workgroup-wide exclusive scan of one value per thread for a BLOCK-thread
+// workgroup.  Every thread must call it.  `tmp` holds BLOCK / 64 words of LDS.
+template <int BLOCK>
+__device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int lane, int wave) {
+    constexpr int WAVES = BLOCK / kWave;
+    const uint32_t inc = wave_inclusive_scan(v, lane);
+    if (lane == kWave - 1) tmp[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+        if (w < wave) before += tmp[w];
+    __syncthreads();
+    return before + inc - v;
+}
+
+// One LSD pass over one tile of BLOCK * ITEMS elements of one row.
+//
+// 1. Load the tile's keys (wave-striped: each wave holds a contiguous run of
+//    the tile and (item, lane) order is input order).
+// 2. Rank stably inside each wave: the lanes sharing a digit are found by
+//    ballots (or by OR-ing lane bits into per-digit masks in LDS); a lane's
+//    rank is the wave's running count of its digit plus the group members at
+//    lower lanes.
+// 3. Per digit: the tile's count (published at once for the look-back; an
+//    inclusive count for a row's first tile), the digit's start in the tile,
+//    each wave's base inside it, and the row's bucket base.
+// 4. Move every key to its slot of the tile's digit order in LDS, then walk
+//    the look-back: the digit's count in earlier tiles of the row, read from
+//    the predecessors' published words until an inclusive count is met.
+// 5. Publish this tile's inclusive counts, then write the keys (and then the
+//    payload through the same slots) with consecutive threads taking
+//    consecutive slots, so each digit run goes to consecutive addresses.
+template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, int MATCH>
+__global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     constexpr uint32_t R = 1u << B;
-    constexpr uint32_t TILE = kBlock * ITEMS;
+    constexpr int WAVES = BLOCK / kWave;
+    constexpr uint32_t TILE = BLOCK * ITEMS;
+    static_assert(BLOCK % kWave == 0 && BLOCK >= static_cast<int>(R), "one thread per digit");
+    static_assert(MATCH != kMatchLds || WAVES * R * 8 <= TILE * 4, "match masks must fit in the tile buffer");
     using Stored = typename KeyTraits<KK>::Stored;
     using St = Status<W>;
 
-    __shared__ uint32_t s_buf[TILE];          // tile in digit order: keys, then payload
-    __shared__ uint32_t s_cnt[kWaves][R];     // per-wave digit counts, then per-wave bases
+    // s_buf holds the tile in digit order (keys, then payload); during the
+    // ranking its front holds the per-wave digit masks of the LDS matching.
+    __shared__ uint32_t s_buf[TILE];
+    __shared__ uint32_t s_cnt[WAVES][R];      // per-wave digit counts, then per-wave bases
     __shared__ uint32_t s_goff[R];            // output index of digit run start minus local start
-    __shared__ uint32_t s_tmp[kWaves];
+    __shared__ uint8_t s_dig[PK != kPayNone ? TILE : 1];  // digit of each slot, for the payload
+    __shared__ uint32_t s_tmp[WAVES];
     __shared__ uint32_t s_ticket;
-    __shared__ unsigned long long s_match[MATCH == kMatchLds ? kWaves : 1][MATCH == kMatchLds ? R : 1];
+    auto s_match = reinterpret_cast<unsigned long long (*)[R]>(s_buf);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    // 64-bit look-back words also mark rows too long for 32-bit buffer offsets
+    constexpr bool kWide = sizeof(W) == 8;
 
-    for (uint32_t i = tid; i < kWaves * R; i += kBlock) (&s_cnt[0][0])[i] = 0u;
+    for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
     if constexpr (MATCH == kMatchLds)
-        for (uint32_t i = tid; i < kWaves * R; i += kBlock) (&s_match[0][0])[i] = 0ull;
+        for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_match[0][0])[i] = 0ull;
     if (tid == 0) s_ticket = atomicAdd(a.tile_counter, 1u);
     __syncthreads();
 
@@ -185,32 +267,17 @@ __global__ __launch_bounds__(kBlock) void sweep_kernel(SweepArgs a) {
 
     const Stored *kin = static_cast<const Stored *>(a.keys_in) + row_base + tile_start;
     const uint32_t wbase = static_cast<uint32_t>(wave) * kWave * ITEMS;
+    const __amdgpu_buffer_rsrc_t kin_rsrc = make_rsrc(kin, valid * sizeof(Stored));
 
-    // Wave-striped load: item j of lane l is tile element wbase + j*64 + l, so
-    // (item, lane) order is input order inside each wave.
+    // 1. Keys.  Elements past the end of the row read as 0 and take the
+    // largest digit: last in input order, they rank after every real key of
+    // that digit and are never written.
     uint32_t key[ITEMS];
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const uint32_t p = wbase + j * kWave + lane;
-        key[j] = (p < valid) ? static_cast<uint32_t>(kin[p]) : 0u;
-    }
-    uint32_t val[ITEMS];
-    if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
-        const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t p = wbase + j * kWave + lane;
-            val[j] = (p < valid) ? vin[p] : 0u;
-        }
-    }
+    for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, wbase + j * kWave + lane);
 
-    // Stable rank inside the wave.  For item j, the lanes holding the same
-    // digit form a group (found by ballots, or by OR-ing each lane's bit into a
-    // per-digit mask in LDS); a lane's rank is the wave's running count of the
-    // digit plus the group members at lower lanes, and the group's lowest lane
-    // advances the running count (and clears the mask).  Elements past the end
-    // of the row take the largest digit; being last in input order they rank
-    // after every real key of that digit and are never written.
+    // 2. Stable rank inside the wave; the group's lowest lane advances the
+    // running count (and clears the mask).
     const uint64_t lane_bit = 1ull << lane;
     uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's digit
 #pragma unroll
@@ -228,6 +295,7 @@ __global__ __launch_bounds__(kBlock) void sweep_kernel(SweepArgs a) {
         const uint32_t below = count_below(m);
         const uint32_t before = s_cnt[wave][d];
         rank[j] = (d << 16) | (before + below);
+        pin(rank[j]);
         if (below == 0u) {
             s_cnt[wave][d] = before + static_cast<uint32_t>(__popcll(m));
             if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
@@ -235,36 +303,33 @@ __global__ __launch_bounds__(kBlock) void sweep_kernel(SweepArgs a) {
     }
     __syncthreads();
 
-    // Digit d is owned by thread d: the tile's count of d, the waves' bases,
-    // and the row's bucket base (exclusive scan of the pass histogram).
+    // 3. Digit d is owned by thread d.
     uint32_t count = 0u;
     if (tid < static_cast<int>(R)) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < WAVES; ++w) {
             const uint32_t c = s_cnt[w][tid];
             s_cnt[w][tid] = count;
             count += c;
         }
     }
-    // Publish this tile's own counts as early as possible.  Padding elements
-    // are not part of the count of the last digit.
-    uint32_t real = count;
+    uint32_t real = count;  // padding is not part of the count of the last digit
     if (tid == static_cast<int>(R) - 1) real -= TILE - valid;
     W *status = static_cast<W *>(a.status) + static_cast<uint64_t>(t) * R;
     if (tid < static_cast<int>(R))
         publish(status + tid, static_cast<W>((tile_in_row == 0 ? St::kInclusive : St::kAggregate) |
                                              static_cast<W>(real)));
-
-    const uint32_t local_start = block_exclusive_scan(count, s_tmp, lane, wave);
-    const uint32_t hcount = (tid < static_cast<int>(R)) ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
-    const uint32_t bucket_base = block_exclusive_scan(hcount, s_tmp, lane, wave);
+    const uint32_t local_start = block_exclusive_scan_n<BLOCK>(count, s_tmp, lane, wave);
+    const uint32_t hcount = (tid < static_cast<int>(R))
+        ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
+    const uint32_t bucket_base = block_exclusive_scan_n<BLOCK>(hcount, s_tmp, lane, wave);
     if (tid < static_cast<int>(R)) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) s_cnt[w][tid] += local_start;
+        for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
     }
     __syncthreads();
 
-    // Local reorder: each key goes to its slot in the tile's digit order.
+    // 4. Local reorder.
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const uint32_t d = rank[j] >> 16;
@@ -273,43 +338,84 @@ __global__ __launch_bounds__(kBlock) void sweep_kernel(SweepArgs a) {
         rank[j] = slot;
     }
 
-    // Decoupled look-back: the count of digit d in all earlier tiles of the row.
-    if (tid < static_cast<int>(R)) {
+    // Payload loads go out now, with the keys out of the registers, and are
+    // in flight while the look-back waits.
+    uint32_t val[ITEMS];
+    if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
+        const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
+        const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
+    }
+
+    // Look-back walk, one thread per digit.  Each round trip a lane reads its
+    // digit's words of the next kLookback predecessors (nearest first) and adds
+    // counts until an inclusive count or an unpublished word.  Lanes of a wave
+    // walk together; when none of a wave's lanes finds anything published, one
+    // lane polls a single word (with a short sleep) until the predecessor has
+    // published, instead of all of them re-reading memory.  The row's first
+    // tile publishes an inclusive count at once, so no walk leaves the row.
+    {
         W excl = 0;
-        if (tile_in_row != 0) {
-            const W *look = static_cast<const W *>(a.status) + static_cast<uint64_t>(t - 1u) * R + tid;
-            for (;;) {
-                const W s = observe(look);
-                const W flag = s & ~St::kMask;
-                if (flag == 0) {
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                excl += s & St::kMask;
-                if (flag == St::kInclusive) break;
-                look -= R;
+        bool done = tile_in_row == 0 || tid >= static_cast<int>(R);
+        uint32_t back = 1;  // the next predecessor to consume is tile t - back
+        const W *row_status = static_cast<const W *>(a.status) + tid;
+        for (;;) {
+            const uint64_t walking = __builtin_amdgcn_ballot_w64(!done);
+            if (walking == 0) break;
+            W sv[kLookback];
+#pragma unroll
+            for (int i = 0; i < kLookback; ++i)
+                sv[i] = (!done && back + i <= tile_in_row)
+                    ? observe(row_status + static_cast<uint64_t>(t - back - i) * R) : W(0);
+            uint32_t used = 0;
+#pragma unroll
+            for (int i = 0; i < kLookback; ++i) {
+                const W flag = sv[i] & ~St::kMask;
+                if (done || used != static_cast<uint32_t>(i) || flag == 0) break;
+                excl += sv[i] & St::kMask;
+                used = i + 1;
+                done = flag == St::kInclusive;
             }
-            publish(status + tid, static_cast<W>(St::kInclusive | (excl + real)));
+            back += used;
+            if (__builtin_amdgcn_ballot_w64(used != 0) == 0) {
+                const int leader = __builtin_ctzll(walking);
+                const W *word = row_status + static_cast<uint64_t>(t - back) * R;
+                for (;;) {
+                    __builtin_amdgcn_s_sleep(2);
+                    W pv = 0;
+                    if (lane == leader) pv = observe(word);
+                    if (__builtin_amdgcn_ballot_w64(lane == leader && (pv & ~St::kMask) != 0) != 0) break;
+                }
+            }
         }
-        s_goff[tid] = bucket_base + static_cast<uint32_t>(excl) - local_start;
-        if (a.status_next != nullptr)
-            static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
+        if (tid < static_cast<int>(R)) {
+            if (tile_in_row != 0)
+                publish(status + tid, static_cast<W>(St::kInclusive | (excl + real)));
+            s_goff[tid] = bucket_base + static_cast<uint32_t>(excl) - local_start;
+            if (a.status_next != nullptr)
+                static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
+        }
     }
     __syncthreads();
 
-    // Write the keys: consecutive threads take consecutive slots, so each
-    // digit run of the tile is written to consecutive addresses.
+    // 5. Keys out: slot k goes to s_goff[d] + k.  That is below row_len for
+    // every real element; the range check of the buffer store only keeps a
+    // logic error from becoming a stray store.
     Stored *kout = static_cast<Stored *>(a.keys_out) + row_base;
-    uint32_t dst[ITEMS];
+    const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t k = i * kBlock + tid;
+        const uint32_t k = i * BLOCK + tid;
         const uint32_t v = s_buf[k];
         const uint32_t d = (KeyTraits<KK>::key(v, a.flip) >> a.shift) & a.digit_mask;
-        dst[i] = s_goff[d] + k;
-        // dst < row_len holds for every real element; the test only keeps a
-        // logic error from turning into a stray store
-        if (k < valid && dst[i] < a.row_len) kout[dst[i]] = static_cast<Stored>(v);
+        if constexpr (PK != kPayNone) s_dig[k] = static_cast<uint8_t>(d);
+        const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
+        if constexpr (kWide) {
+            if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
+        } else {
+            BufIO<Stored>::store(kout_rsrc, dst, v);
+        }
     }
 
     if constexpr (PK != kPayNone) {
@@ -322,14 +428,17 @@ __global__ __launch_bounds__(kBlock) void sweep_kernel(SweepArgs a) {
             s_buf[rank[j]] = v;
         }
         __syncthreads();
+        using OutT = typename std::conditional<PK == kPayIdxLast, int64_t, uint32_t>::type;
+        OutT *vout = static_cast<OutT *>(a.vals_out) + row_base;
+        const __amdgpu_buffer_rsrc_t vout_rsrc = make_rsrc(vout, kWide ? 0u : a.row_len * sizeof(OutT));
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const uint32_t k = i * kBlock + tid;
-            if (k < valid && dst[i] < a.row_len) {
-                if constexpr (PK == kPayIdxLast)
-                    static_cast<int64_t *>(a.vals_out)[row_base + dst[i]] = static_cast<int64_t>(s_buf[k]);
-                else
-                    static_cast<uint32_t *>(a.vals_out)[row_base + dst[i]] = s_buf[k];
+            const uint32_t k = i * BLOCK + tid;
+            const uint32_t dst = (k < valid) ? s_goff[s_dig[k]] + k : 0xFFFFFFFFu;
+            if constexpr (kWide) {
+                if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_buf[k]);
+            } else {
+                BufIO<OutT>::store(vout_rsrc, dst, s_buf[k]);
             }
         }
     }
@@ -351,25 +460,31 @@ struct HistArgs {
 };
 
 constexpr int kHistMaxCounters = 1024;  // passes * R for every legal (window, b)
+constexpr int kHistCopies = LRS_HIST_COPIES;
 
 // Counts every pass's digit over one chunk of one row in LDS, from one read of
 // the keys with 16-byte loads, then adds the counts to the row's histogram.
+// Lane l counts into copy l % kHistCopies of the counters (copies of one
+// counter sit in consecutive words), so lanes that share a digit mostly hit
+// different LDS banks instead of serialising on one address.
 template <int B, int KK>
 __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t R = 1u << B;
     using Stored = typename KeyTraits<KK>::Stored;
     constexpr uint32_t kPerVec = 16u / sizeof(Stored);
-    __shared__ uint32_t s_h[kHistMaxCounters];
+    constexpr int kUnroll = 4;
+    __shared__ uint32_t s_h[kHistMaxCounters * kHistCopies];
 
     const uint32_t row = blockIdx.x / a.chunks_per_row;
     const uint32_t chunk = blockIdx.x - row * a.chunks_per_row;
     const uint32_t total = a.passes * R;
-    for (uint32_t i = threadIdx.x; i < total; i += kBlock) s_h[i] = 0u;
+    for (uint32_t i = threadIdx.x; i < total * kHistCopies; i += kBlock) s_h[i] = 0u;
     __syncthreads();
 
     const uint32_t lo = chunk * a.chunk;
     const uint32_t hi = min(a.row_len, lo + a.chunk);
     const Stored *base = static_cast<const Stored *>(a.keys) + static_cast<uint64_t>(row) * a.row_len;
+    uint32_t *mine = s_h + (threadIdx.x % kHistCopies);
 
     auto count_key = [&](uint32_t v) {
         const uint32_t k = KeyTraits<KK>::key(v, a.flip);
@@ -377,7 +492,17 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
             const uint32_t shift = a.begin_bit + p * B;
             const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
             const uint32_t d = (k >> shift) & ((1u << width) - 1u);
-            atomicAdd(&s_h[p * R + d], 1u);
+            atomicAdd(mine + (p * R + d) * kHistCopies, 1u);
+        }
+    };
+    auto count_vec = [&](const uint4 &w) {
+        if constexpr (KK == kKeyU32) {
+            count_key(w.x); count_key(w.y); count_key(w.z); count_key(w.w);
+        } else {
+            count_key(w.x & 0xFFFFu); count_key(w.x >> 16);
+            count_key(w.y & 0xFFFFu); count_key(w.y >> 16);
+            count_key(w.z & 0xFFFFu); count_key(w.z >> 16);
+            count_key(w.w & 0xFFFFu); count_key(w.w >> 16);
         }
     };
 
@@ -388,17 +513,15 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     if ((addr & 15u) == 0u) {
         const uint32_t nvec = (hi - lo) / kPerVec;
         const uint4 *v4 = reinterpret_cast<const uint4 *>(base + lo);
-        for (uint32_t q = threadIdx.x; q < nvec; q += kBlock) {
-            const uint4 w = v4[q];
-            if constexpr (KK == kKeyU32) {
-                count_key(w.x); count_key(w.y); count_key(w.z); count_key(w.w);
-            } else {
-                count_key(w.x & 0xFFFFu); count_key(w.x >> 16);
-                count_key(w.y & 0xFFFFu); count_key(w.y >> 16);
-                count_key(w.z & 0xFFFFu); count_key(w.z >> 16);
-                count_key(w.w & 0xFFFFu); count_key(w.w >> 16);
-            }
+        uint32_t q = threadIdx.x;
+        for (; q + (kUnroll - 1) * kBlock < nvec; q += kUnroll * kBlock) {
+            uint4 w[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) w[u] = v4[q + u * kBlock];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) count_vec(w[u]);
         }
+        for (; q < nvec; q += kBlock) count_vec(v4[q]);
         i = lo + nvec * kPerVec;
     }
     for (uint32_t q = i + threadIdx.x; q < hi; q += kBlock) count_key(static_cast<uint32_t>(base[q]));
@@ -406,7 +529,9 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
 
     uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
     for (uint32_t q = threadIdx.x; q < total; q += kBlock) {
-        const uint32_t c = s_h[q];
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < kHistCopies; ++k) c += s_h[q * kHistCopies + k];
         if (a.atomic) {
             if (c) atomicAdd(out + q, c);
         } else {
@@ -438,12 +563,21 @@ __global__ __launch_bounds__(kBlock) void clear_kernel(ClearArgs a) {
     }
 }
 
+// Plain streaming copy, four 16-byte loads in flight per thread.
 __global__ __launch_bounds__(kBlock) void copy_kernel(const uint4 *src, uint4 *dst, uint64_t n16,
                                                       const uint8_t *src_tail, uint8_t *dst_tail,
                                                       uint32_t tail) {
+    constexpr int kUnroll = 4;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n16; i += stride)
-        dst[i] = src[i];
+    uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+        uint4 w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) w[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = w[u];
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
     if (blockIdx.x == 0 && threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 

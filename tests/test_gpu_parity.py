@@ -97,6 +97,22 @@ def test_c3_pairs_reduced_size(dist):
     assert_same(gv, ev, "values")
 
 
+@pytest.mark.parametrize("b,dist", [(8, "uniform"), (4, "and3")])
+def test_large_tile_configuration(b, dist):
+    # enough elements for the largest sweep tile (at least 1024 tiles of 12288)
+    n = 13_000_003
+    keys = workloads.random_u32(4000 + b, n)
+    if dist == "and3":
+        keys &= workloads.random_u32(4100, n) & workloads.random_u32(4200, n)
+    vals = np.arange(n, dtype=np.uint32)
+    log(f"large tiles n={n} b={b} {dist}")
+    ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, b)
+    gk, gv = gpu_pairs(keys, vals, 0, 32, b)
+    assert_same(gk, ek, "keys")
+    assert_same(gv, ev, "values")
+    assert_same(gpu_keys(keys, 0, 32, b), ek, "keys only")
+
+
 def test_pass_by_pass_states():
     # the state after p passes is the stable sort by the low p*b bits of the window
     n = 300_001
