@@ -1,17 +1,23 @@
-"""Benchmark: 2^28 u32 key + u32 value LSD radix sort on one MI355X.
+"""Benchmark: LSD radix sort on one MI355X.
 
-One step = one full sort (clear, all-pass histogram, 4 sweep passes of 8-bit
-digits) of 2^28 seeded synthetic pairs already resident in HBM, out of place
-from an input the loop never writes.  Prints one JSON line.
+Default workload (the headline): 2^28 u32 key + u32 value pairs, value =
+original index, uniform keys, 8-bit digits, 4 passes.  One step = one full
+sort (clear, all-pass histogram, one sweep per pass) of seeded synthetic data
+already resident in HBM, out of place from an input the loop never writes.
+Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--dist uniform|and3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
 
-roofline: the dominant kernel is the sweep pass; its algorithmic traffic is
-16 B per pair (read key + value, write key + value), so
-achieved = 16 * n / (average sweep launch time), against 8 TB/s HBM peak.
-The average launch time comes from HIP events the library records around each
-sweep launch inside the timed region.
+Other workloads (same line format, for the record): c1_keys_1k_4bit,
+c2_keys_4m_4bit, c2_keys_4m_8bit, c3_pairs_2p28_and3, c4_fp16_1024x65536_asc,
+c5_bf16_4096x4096_desc.
+
+roofline: the dominant kernel is the sweep (one LSD pass).  achieved = the
+algorithmic bytes of the sweep launches of one sort (pairs: 16 B per pair per
+pass; keys: 8 B per key per pass; fp16/bf16 rows: 8, 12, ..., 16 B per element
+from the first to the last pass) / their summed duration, from HIP events the
+library records around each sweep launch inside the timed region.
 """
 from __future__ import annotations
 
@@ -25,35 +31,73 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-N = 1 << 28
-DIGIT_BITS = 8
-BYTES_PER_PAIR_PER_PASS = 16
-# HBM bytes per sweep launch of the current sweep kernel (512 x 24 tile, ballot
-# ranking) measured by rocprofv3 FETCH_SIZE and WRITE_SIZE over this benchmark,
-# each scaled by the copy-kernel calibration (x2.0 and x1.0); set to None when
-# the kernel changes until the counters are taken again.
-MEASURED_SWEEP_TRAFFIC = 4_735_635_251
+HEADLINE = "c3_pairs_2p28_uniform"
+# HBM bytes per sweep launch of the current sweep kernel on the headline
+# workload (512 x 24 tile, ballot ranking), measured by rocprofv3 FETCH_SIZE and
+# WRITE_SIZE over this benchmark, each scaled by the copy-kernel calibration
+# (x2.0 and x1.0); set to None when the kernel changes until the counters are
+# taken again.
+MEASURED_SWEEP_TRAFFIC = {HEADLINE: 4_735_635_251}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+WORKLOADS = {
+    "c1_keys_1k_4bit": dict(kind="keys", n=1024, end_bit=12, b=4, desc="1,024 u32 keys uniform in [0,4096), "
+                            "keys only, 4-bit digits, 3 passes (bits 0-11)"),
+    "c2_keys_4m_4bit": dict(kind="keys", n=1 << 22, end_bit=32, b=4, desc="4,194,304 u32 keys, full range, "
+                            "keys only, 4-bit digits, 8 passes"),
+    "c2_keys_4m_8bit": dict(kind="keys", n=1 << 22, end_bit=32, b=8, desc="4,194,304 u32 keys, full range, "
+                            "keys only, 8-bit digits, 4 passes"),
+    "c3_pairs_2p28_uniform": dict(kind="pairs", n=1 << 28, end_bit=32, b=8, dist="uniform",
+                                  desc="2^28 u32 key + u32 value pairs (value = original index), uniform keys, "
+                                       "8-bit digits, 4 LSD passes"),
+    "c3_pairs_2p28_and3": dict(kind="pairs", n=1 << 28, end_bit=32, b=8, dist="and3",
+                               desc="2^28 u32 key + u32 value pairs (value = original index), keys = AND of 3 "
+                                    "uniform words, 8-bit digits, 4 LSD passes"),
+    "c4_fp16_1024x65536_asc": dict(kind="rows", rows=1024, cols=65536, dtype="fp16", descending=False, b=4,
+                                   desc="fp16 (1024, 65536) N(0,1) rows, ascending, int64 column index, 4-bit "
+                                        "digits, 4 passes"),
+    "c5_bf16_4096x4096_desc": dict(kind="rows", rows=4096, cols=4096, dtype="bf16", descending=True, b=8,
+                                   desc="bf16 (4096, 4096) 64-level N(0,1) rows, descending, int64 column index, "
+                                        "8-bit digits, 2 passes"),
+}
+
+
+def sweep_bytes(w) -> int:
+    """Algorithmic bytes of all sweep launches of one sort of workload w."""
+    P = -(-w["end_bit"] // w["b"]) if w["kind"] != "rows" else 16 // w["b"]
+    if w["kind"] == "keys":
+        return 8 * w["n"] * P
+    if w["kind"] == "pairs":
+        return 16 * w["n"] * P
+    n = w["rows"] * w["cols"]
+    total = 0
+    for p in range(P):
+        read = 2 + (4 if p > 0 else 0)          # 16-bit pattern (+ u32 index after the first pass)
+        write = 2 + (8 if p == P - 1 else 4)    # pattern + u32 index (int64 on the last pass)
+        total += read + write
+    return n * total
+
+
 def cpu_baseline(min_seconds: float = 10.0, max_runs: int = 3):
-    """Single-threaded oracle on the benchmark's own input, repeated until at
-    least min_seconds of CPU work (at most max_runs sorts)."""
+    """Single-threaded oracle on the headline workload's own input, repeated
+    until at least min_seconds of CPU work (at most max_runs sorts)."""
     import oracle
     import workloads
 
-    keys, vals = workloads.pairs_c3(N, "uniform")
+    n = 1 << 28
+    keys, vals = workloads.pairs_c3(n, "uniform")
     runs, total = 0, 0.0
     while runs < max_runs and (runs == 0 or total < min_seconds):
         t0 = time.perf_counter()
-        oracle.radix_sort_pairs(keys, vals, 0, 32, DIGIT_BITS)
+        oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
         total += time.perf_counter() - t0
         runs += 1
     return {
-        "value": round(runs * N / total / 1e9, 5),
+        "value": round(runs * n / total / 1e9, 5),
         "unit": "Gkeys/s",
         "cores": 1,
         "kind": "oracle",
@@ -68,13 +112,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--dist", default="uniform", choices=["uniform", "and3"])
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--dist", default=None, choices=["uniform", "and3"],
+                    help="shorthand for the 2^28-pair workload with this key distribution")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    name = args.workload
+    if args.dist is not None:
+        name = f"c3_pairs_2p28_{args.dist}"
+    w = WORKLOADS[name]
 
     import numpy as np
     import torch
@@ -86,18 +136,49 @@ def main():
     lrs.load_library()
     dev = torch.device("cuda:0")
 
-    log(f"generating {N} pairs ({args.dist})")
-    keys, vals = workloads.pairs_c3(N, args.dist)
-    k_in = torch.from_numpy(keys.view(np.int32)).to(dev)
-    v_in = torch.from_numpy(vals.view(np.int32)).to(dev)
-    del keys, vals
-    k_out = torch.empty_like(k_in)
-    v_out = torch.empty_like(v_in)
-    ws = torch.empty(lrs.radix_sort_workspace_size(N, 0, 32, DIGIT_BITS, True), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
+    log(f"generating {name}")
+    if w["kind"] == "keys":
+        keys = workloads.keys_c1(w["n"]) if w["n"] == 1024 else workloads.keys_c2(w["n"])
+        k_in = torch.from_numpy(keys.view(np.int32)).to(dev)
+        n_keys = w["n"]
+        k_out = torch.empty_like(k_in)
+        ws = torch.empty(max(1, lrs.radix_sort_workspace_size(n_keys, 0, w["end_bit"], w["b"], False)),
+                         dtype=torch.uint8, device=dev)
 
-    def step():
-        lrs.radix_sort_pairs(k_in, v_in, 0, 32, DIGIT_BITS, keys_out=k_out, values_out=v_out, workspace=ws)
+        def step():
+            lrs.radix_sort_keys(k_in, 0, w["end_bit"], w["b"], out=k_out, workspace=ws)
+        scratch = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        copy_pair = (scratch[: 1 << 27], scratch[1 << 27:])
+    elif w["kind"] == "pairs":
+        keys, vals = workloads.pairs_c3(w["n"], w["dist"])
+        k_in = torch.from_numpy(keys.view(np.int32)).to(dev)
+        v_in = torch.from_numpy(vals.view(np.int32)).to(dev)
+        del keys, vals
+        n_keys = w["n"]
+        k_out = torch.empty_like(k_in)
+        v_out = torch.empty_like(v_in)
+        ws = torch.empty(lrs.radix_sort_workspace_size(n_keys, 0, 32, w["b"], True), dtype=torch.uint8, device=dev)
+
+        def step():
+            lrs.radix_sort_pairs(k_in, v_in, 0, 32, w["b"], keys_out=k_out, values_out=v_out, workspace=ws)
+        copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
+    else:
+        bits = workloads.matrix_c4(w["rows"], w["cols"]) if w["dtype"] == "fp16" else workloads.matrix_c5(
+            w["rows"], w["cols"])
+        x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16 if w["dtype"] == "fp16"
+                                                                else torch.bfloat16)
+        n_keys = w["rows"] * w["cols"]
+        vo = torch.empty_like(x)
+        io = torch.empty((w["rows"], w["cols"]), dtype=torch.int64, device=dev)
+        ws = torch.empty(lrs.segmented_row_sort_workspace_size(w["rows"], w["cols"], w["b"]), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            lrs.segmented_row_sort(x, w["descending"], w["b"], values_out=vo, indices_out=io, workspace=ws)
+        scratch = io.view(torch.uint8).reshape(-1)
+        half = scratch.numel() // 2 // 16 * 16
+        copy_pair = (scratch[:half], scratch[half:2 * half])
+    torch.cuda.synchronize()
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -113,29 +194,28 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gkeys = N / (ms_per_step / 1e3) / 1e9
+    gkeys = n_keys / (ms_per_step / 1e3) / 1e9
 
-    passes = 32 // DIGIT_BITS
-    sweep_ms = kt.ms["sweep"] / max(kt.launches["sweep"], 1)
+    sweep_launches = max(kt.launches["sweep"], 1)
+    sweep_ms_total = kt.ms["sweep"] / args.steps
+    sweep_ms = kt.ms["sweep"] / sweep_launches
     hist_ms = kt.ms["histogram"] / max(kt.launches["histogram"], 1)
     clear_ms = kt.ms["clear"] / max(kt.launches["clear"], 1)
-    sweep_bytes = BYTES_PER_PAIR_PER_PASS * N
-    achieved = sweep_bytes / (sweep_ms / 1e3) / 1e9
+    launches_per_sort = sweep_launches // args.steps
+    bytes_sort = sweep_bytes(w)
+    achieved = bytes_sort / (sweep_ms_total / 1e3) / 1e9
 
-    # copy yardstick: 2 GiB -> 2 GiB with the library's copy kernel
-    src = k_in.view(torch.uint8)
-    dst = k_out.view(torch.uint8)
+    # copy yardstick: the library's streaming copy kernel between two resident
+    # buffers (the 1 GiB key buffers for the 2^28-pair workloads)
     with lrs.KernelTimer() as ct:
         for _ in range(5):
-            lrs.copy_probe(src, dst)
+            lrs.copy_probe(copy_pair[0], copy_pair[1])
     copy_ms = ct.ms["copy"] / max(ct.launches["copy"], 1)
-    copy_gbs = 2 * src.numel() / (copy_ms / 1e3) / 1e9
-    log(f"sort {ms_per_step:.3f} ms/step, {gkeys:.2f} Gkeys/s; sweep {sweep_ms:.3f} ms/pass = "
-        f"{achieved:.0f} GB/s; histogram {hist_ms:.3f} ms; clear {clear_ms:.3f} ms; copy {copy_gbs:.0f} GB/s")
+    copy_gbs = 2 * copy_pair[0].numel() / (copy_ms / 1e3) / 1e9
+    log(f"{name}: sort {ms_per_step:.4f} ms/step, {gkeys:.3f} Gkeys/s; sweep {sweep_ms:.4f} ms/launch "
+        f"x {launches_per_sort} = {achieved:.0f} GB/s; histogram {hist_ms:.4f} ms; clear {clear_ms:.4f} ms; "
+        f"copy {copy_gbs:.0f} GB/s")
 
-    traffic = None
-    if MEASURED_SWEEP_TRAFFIC is not None:
-        traffic = MEASURED_SWEEP_TRAFFIC
     result = {
         "metric": "Gkeys/s and achieved HBM GB/s (% of peak), 2^28 u32 key-value radix sort",
         "value": round(gkeys, 4),
@@ -147,22 +227,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32",
+        "dtype": "u16" if w["kind"] == "rows" else "u32",
         "data": "synthetic",
-        "config": {
-            "workload": f"2^28 u32 key + u32 value pairs (value = original index), {args.dist} keys, "
-                        f"8-bit digits, 4 LSD passes",
-            "n": N, "digit_bits": DIGIT_BITS, "passes": passes, "key_distribution": args.dist,
-        },
+        "config": {"workload": w["desc"], "name": name, "n": n_keys, "digit_bits": w["b"],
+                   "passes": launches_per_sort},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "sweep_kernel<8-bit digit, u32 key, u32 value> (one LSD pass)",
-            "bytes_per_launch": sweep_bytes,
+            "traffic": MEASURED_SWEEP_TRAFFIC.get(name),
+            "kernel": "sweep_kernel (one LSD pass)",
+            "bytes_per_launch": bytes_sort // max(launches_per_sort, 1),
             "avg_launch_ms": round(sweep_ms, 4),
         },
         "per_kernel_ms": {"clear": round(clear_ms, 4), "histogram": round(hist_ms, 4),
@@ -171,9 +248,9 @@ def main():
         "copy_probe_gbs": round(copy_gbs, 1),
         "frac_of_copy": round(achieved / copy_gbs, 4),
     }
-    del k_in, v_in, k_out, v_out, ws
+    del ws, copy_pair
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if name == HEADLINE and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
