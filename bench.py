@@ -17,7 +17,10 @@ roofline: the dominant kernel is the sweep (one LSD pass).  achieved = the
 algorithmic bytes of the sweep launches of one sort (pairs: 16 B per pair per
 pass; keys: 8 B per key per pass; fp16/bf16 rows: 8, 12, ..., 16 B per element
 from the first to the last pass) / their summed duration, from HIP events the
-library records around each sweep launch inside the timed region.
+library records around each sweep launch inside the timed region.  Rows of at
+most 8192 elements are sorted by one whole-row resident launch instead (read
+once, write once: 8 B/key, 16 B/pair, 12 B per fp16/bf16 element with its
+int64 index).
 """
 from __future__ import annotations
 
@@ -80,6 +83,15 @@ def sweep_bytes(w) -> int:
         write = 2 + (8 if p == P - 1 else 4)    # pattern + u32 index (int64 on the last pass)
         total += read + write
     return n * total
+
+
+def resident_bytes(w) -> int:
+    """Algorithmic bytes of one whole-row resident sort: read once, write once."""
+    if w["kind"] == "keys":
+        return 8 * w["n"]
+    if w["kind"] == "pairs":
+        return 16 * w["n"]
+    return 12 * w["rows"] * w["cols"]  # 16-bit pattern in; pattern + int64 index out
 
 
 def cpu_baseline(min_seconds: float = 10.0, max_runs: int = 3):
@@ -196,14 +208,19 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     gkeys = n_keys / (ms_per_step / 1e3) / 1e9
 
-    sweep_launches = max(kt.launches["sweep"], 1)
-    sweep_ms_total = kt.ms["sweep"] / args.steps
-    sweep_ms = kt.ms["sweep"] / sweep_launches
+    # Inputs of at most 8192 elements per row are sorted by one whole-row
+    # resident launch (one read, one write); longer ones by one sweep per pass.
+    resident = kt.launches["resident"] > 0
+    kind = "resident" if resident else "sweep"
+    dom_launches = max(kt.launches[kind], 1)
+    dom_ms_total = kt.ms[kind] / args.steps
+    dom_ms = kt.ms[kind] / dom_launches
     hist_ms = kt.ms["histogram"] / max(kt.launches["histogram"], 1)
     clear_ms = kt.ms["clear"] / max(kt.launches["clear"], 1)
-    launches_per_sort = sweep_launches // args.steps
-    bytes_sort = sweep_bytes(w)
-    achieved = bytes_sort / (sweep_ms_total / 1e3) / 1e9
+    launches_per_sort = dom_launches // args.steps
+    bytes_sort = resident_bytes(w) if resident else sweep_bytes(w)
+    achieved = bytes_sort / (dom_ms_total / 1e3) / 1e9
+    sweep_ms = dom_ms
 
     # copy yardstick: the library's streaming copy kernel between two resident
     # buffers (the 1 GiB key buffers for the 2^28-pair workloads)
@@ -212,7 +229,7 @@ def main():
             lrs.copy_probe(copy_pair[0], copy_pair[1])
     copy_ms = ct.ms["copy"] / max(ct.launches["copy"], 1)
     copy_gbs = 2 * copy_pair[0].numel() / (copy_ms / 1e3) / 1e9
-    log(f"{name}: sort {ms_per_step:.4f} ms/step, {gkeys:.3f} Gkeys/s; sweep {sweep_ms:.4f} ms/launch "
+    log(f"{name}: sort {ms_per_step:.4f} ms/step, {gkeys:.3f} Gkeys/s; {kind} {sweep_ms:.4f} ms/launch "
         f"x {launches_per_sort} = {achieved:.0f} GB/s; histogram {hist_ms:.4f} ms; clear {clear_ms:.4f} ms; "
         f"copy {copy_gbs:.0f} GB/s")
 
@@ -238,12 +255,14 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": MEASURED_SWEEP_TRAFFIC.get(name),
-            "kernel": "sweep_kernel (one LSD pass)",
+            "kernel": "resident_sort_kernel (whole row, all passes in LDS)" if resident
+                      else "sweep_kernel (one LSD pass)",
             "bytes_per_launch": bytes_sort // max(launches_per_sort, 1),
             "avg_launch_ms": round(sweep_ms, 4),
         },
-        "per_kernel_ms": {"clear": round(clear_ms, 4), "histogram": round(hist_ms, 4),
-                          "sweep_per_pass": round(sweep_ms, 4)},
+        "per_kernel_ms": ({"resident_sort": round(sweep_ms, 4)} if resident else
+                          {"clear": round(clear_ms, 4), "histogram": round(hist_ms, 4),
+                           "sweep_per_pass": round(sweep_ms, 4)}),
         "hbm_gbs_per_pass": round(achieved, 1),
         "copy_probe_gbs": round(copy_gbs, 1),
         "frac_of_copy": round(achieved / copy_gbs, 4),

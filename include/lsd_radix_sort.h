@@ -22,7 +22,9 @@
  *  - The caller provides scratch device memory (`workspace`) of at least the
  *    size the matching *_workspace_size() call returns; its contents on entry
  *    do not matter and on return are unspecified.  Calls that share a
- *    workspace must be ordered on one stream.
+ *    workspace must be ordered on one stream.  Inputs whose rows hold at most
+ *    8192 elements are sorted whole inside one workgroup and need no
+ *    workspace (the size is 0 and workspace may be NULL).
  *  - The result of a sort is unique: a stable sort by the key, ties in input
  *    order, payload travelling with its key.
  *  - Return value: LRS_OK or an lrs_status code.  Argument errors are reported
@@ -138,8 +140,9 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
  * kernel the library enqueues is bracketed by HIP events on its stream.
  * radix_sort_timing_end() waits for those events and reports, per kernel kind
  * (0 = workspace clear, 1 = digit histogram, 2 = sweep/scatter pass,
- * 3 = copy probe), the summed milliseconds and the number of launches, then
- * stops recording.  Arrays have 4 entries.  At most 65536 launches are timed.
+ * 3 = copy probe, 4 = whole-row resident sort), the summed milliseconds and
+ * the number of launches, then stops recording.  Arrays have 5 entries.  At
+ * most 65536 launches are timed.
  * Not thread-safe; for benchmarking only.
  */
 int radix_sort_timing_begin(void);

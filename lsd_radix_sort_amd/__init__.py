@@ -212,17 +212,17 @@ class KernelTimer:
     """Context manager: HIP-event times of every kernel the library enqueues inside it.
 
     After exit, ``ms`` and ``launches`` hold per-kind sums for the kinds
-    "clear", "histogram", "sweep", "copy".
+    "clear", "histogram", "sweep", "copy", "resident".
     """
-    KINDS = ("clear", "histogram", "sweep", "copy")
+    KINDS = ("clear", "histogram", "sweep", "copy", "resident")
 
     def __enter__(self):
         _check(load_library().radix_sort_timing_begin(), "timing_begin")
         return self
 
     def __exit__(self, *exc):
-        ms = (ctypes.c_double * 4)()
-        nl = (ctypes.c_int * 4)()
+        ms = (ctypes.c_double * 5)()
+        nl = (ctypes.c_int * 5)()
         _check(load_library().radix_sort_timing_end(ms, nl), "timing_end")
         self.ms = dict(zip(self.KINDS, list(ms)))
         self.launches = dict(zip(self.KINDS, list(nl)))

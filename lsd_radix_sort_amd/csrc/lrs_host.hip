@@ -33,6 +33,8 @@ struct TileCfg {
 constexpr TileCfg kTileCfgs[3] = {
     {256, 16, 4096}, {512, 16, 8192}, {kSweepBlock, LRS_SWEEP_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_ITEMS}};
 constexpr uint64_t kMinTiles = 1024;  // about four tiles per CU
+// Rows up to this length are sorted whole inside one workgroup's LDS.
+constexpr uint64_t kResidentMax = 8192;
 
 int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
     for (int c = 2; c >= 1; --c) {
@@ -97,6 +99,7 @@ struct Plan {
     int b = 8;
     int begin_bit = 0;
     int end_bit = 32;
+    bool resident = false;          // whole row sorted in one workgroup, no workspace
     int tile_cfg = 0;
     uint32_t tiles_per_row = 0;
     uint64_t num_tiles = 0;
@@ -165,6 +168,10 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
         }
     }
     p.total = off;
+    if (row_len <= kResidentMax) {
+        p.resident = true;
+        p.total = 0;
+    }
     return p;
 }
 
@@ -244,6 +251,33 @@ hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t 
     }
 }
 
+template <int B, int KK, int PK>
+hipError_t launch_resident_b(const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s) {
+    // one workgroup per row; the smallest shape that holds the row
+    const dim3 grid(static_cast<uint32_t>(rows));
+    if (row_len <= 1024)
+        resident_sort_kernel<B, 4, 256, KK, PK><<<grid, 256, 0, s>>>(a);
+    else if (row_len <= 4096)
+        resident_sort_kernel<B, 16, 256, KK, PK><<<grid, 256, 0, s>>>(a);
+    else
+        resident_sort_kernel<B, 16, 512, KK, PK><<<grid, 512, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int KK, int PK>
+hipError_t launch_resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s) {
+    TimedLaunch t(4, s);
+    hipError_t e;
+    switch (b) {
+        case 1: e = launch_resident_b<1, KK, PK>(a, rows, row_len, s); break;
+        case 2: e = launch_resident_b<2, KK, PK>(a, rows, row_len, s); break;
+        case 4: e = launch_resident_b<4, KK, PK>(a, rows, row_len, s); break;
+        default: e = launch_resident_b<8, KK, PK>(a, rows, row_len, s); break;
+    }
+    t.done();
+    return e;
+}
+
 hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, hipStream_t s) {
     ClearArgs c{};
     c.p[0] = need_hist ? reinterpret_cast<uint32_t *>(ws + p.off_hist) : nullptr;
@@ -315,12 +349,12 @@ int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint3
     if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
     if (n == 0) return LRS_OK;
-    if (!keys_in || !keys_out || (pairs && (!vals_in || !vals_out)) || !workspace)
+    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0);
+    if (!keys_in || !keys_out || (pairs && (!vals_in || !vals_out)) || (p.total && !workspace))
         return LRS_ERR_NULL_POINTER;
     if (misaligned(keys_in, 4) || misaligned(keys_out, 4) || misaligned(workspace, 256) ||
         (pairs && (misaligned(vals_in, 4) || misaligned(vals_out, 4))))
         return LRS_ERR_ALIGNMENT;
-    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0);
     if (ws_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
     const uint64_t kb = 4 * n;
     if (overlaps(keys_out, kb, keys_in, kb) || overlaps(keys_out, kb, workspace, p.total) ||
@@ -330,6 +364,19 @@ int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint3
         return LRS_ERR_ALIASING;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.resident) {
+        ResidentArgs r{};
+        r.keys_in = keys_in;
+        r.keys_out = keys_out;
+        r.vals_in = vals_in;
+        r.vals_out = vals_out;
+        r.row_len = static_cast<uint32_t>(n);
+        r.begin_bit = static_cast<uint32_t>(begin_bit);
+        r.end_bit = static_cast<uint32_t>(end_bit);
+        const hipError_t e = pairs ? launch_resident<kKeyU32, kResU32>(b, r, 1, n, s)
+                                   : launch_resident<kKeyU32, kResNone>(b, r, 1, n, s);
+        return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
@@ -408,11 +455,11 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
         (rows > 0 && static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40)))
         return LRS_ERR_SIZE;
     if (rows == 0 || n == 0) return LRS_OK;
-    if (!vals_in || !vals_out || !idx_out || !workspace) return LRS_ERR_NULL_POINTER;
+    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2);
+    if (!vals_in || !vals_out || !idx_out || (p.total && !workspace)) return LRS_ERR_NULL_POINTER;
     if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(idx_out, 8) ||
         misaligned(workspace, 256))
         return LRS_ERR_ALIGNMENT;
-    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2);
     if (p.num_tiles > 0x7FFFFFFFull || p.rows * p.hist_chunks_per_row > 0x7FFFFFFFull) return LRS_ERR_SIZE;
     if (workspace_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
     const uint64_t cnt = static_cast<uint64_t>(rows) * n;
@@ -422,8 +469,21 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
         return LRS_ERR_ALIASING;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
     const uint32_t flip = descending ? 0xFFFFu : 0u;
+    if (p.resident) {
+        if (rows > 0x7FFFFFFF) return LRS_ERR_SIZE;
+        ResidentArgs r{};
+        r.keys_in = vals_in;
+        r.keys_out = vals_out;
+        r.vals_out = idx_out;
+        r.row_len = static_cast<uint32_t>(n);
+        r.begin_bit = 0;
+        r.end_bit = 16;
+        r.flip = flip;
+        const hipError_t e = launch_resident<kKeyF16, kResIndex>(digit_bits, r, rows, n, s);
+        return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    }
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
     if (launch_histogram(p, vals_in, hist, kKeyF16, flip, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
@@ -509,7 +569,7 @@ int radix_sort_timing_begin(void) {
 }
 
 int radix_sort_timing_end(double *ms_by_kind, int *launches_by_kind) {
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 5; ++k) {
         if (ms_by_kind) ms_by_kind[k] = 0.0;
         if (launches_by_kind) launches_by_kind[k] = 0;
     }

@@ -444,6 +444,148 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     }
 }
 
+// ------------------------------------------------- whole-row resident sort
+
+struct ResidentArgs {
+    const void *keys_in;
+    void *keys_out;
+    const void *vals_in;     // u32 payload (pairs), else unused
+    void *vals_out;          // u32 payload (pairs) or int64 column index (rows)
+    uint32_t row_len;        // elements per row, at most BLOCK * ITEMS
+    uint32_t begin_bit;
+    uint32_t end_bit;
+    uint32_t flip;           // 0xFFFF for descending 16-bit float keys, else 0
+};
+
+// Payload of the resident sort.
+enum ResPay : int { kResNone = 0, kResU32 = 1, kResIndex = 2 };
+
+// Sorts one row (one workgroup per row) by all of its LSD passes inside LDS:
+// the row is read once, every pass ranks it stably (wave ballots, per-wave
+// digit counts, local digit starts) and moves keys and payload between two LDS
+// buffers, and the result is written once.  The ranking is the one of
+// sweep_kernel; with the whole row in one tile the earlier-tile counts are
+// zero and the digit starts are the row's bucket bases, so no histogram, scan
+// or look-back is needed (one launch in all).
+template <int B, int ITEMS, int BLOCK, int KK, int PK>
+__global__ __launch_bounds__(BLOCK) void resident_sort_kernel(ResidentArgs a) {
+    constexpr uint32_t R = 1u << B;
+    constexpr int WAVES = BLOCK / kWave;
+    constexpr uint32_t TILE = BLOCK * ITEMS;
+    static_assert(BLOCK % kWave == 0 && BLOCK >= static_cast<int>(R), "one thread per digit");
+    using Stored = typename KeyTraits<KK>::Stored;
+
+    __shared__ Stored s_key[2][TILE];
+    __shared__ uint32_t s_val[PK != kResNone ? 2 : 1][PK != kResNone ? TILE : 1];
+    __shared__ uint32_t s_cnt[WAVES][R];
+    __shared__ uint32_t s_tmp[WAVES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t row = blockIdx.x;
+    const uint32_t n = a.row_len;
+    const uint64_t row_base = static_cast<uint64_t>(row) * n;
+    const uint32_t wbase = static_cast<uint32_t>(wave) * kWave * ITEMS;
+
+    uint32_t key[ITEMS];
+    uint32_t val[ITEMS];
+    {
+        const __amdgpu_buffer_rsrc_t kin = make_rsrc(static_cast<const Stored *>(a.keys_in) + row_base, n * sizeof(Stored));
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin, wbase + j * kWave + lane);
+        if constexpr (PK == kResU32) {
+            const __amdgpu_buffer_rsrc_t vin = make_rsrc(static_cast<const uint32_t *>(a.vals_in) + row_base, n * 4u);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin, wbase + j * kWave + lane);
+        } else if constexpr (PK == kResIndex) {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) val[j] = wbase + j * kWave + lane;
+        }
+    }
+
+    int cur = 0;
+    for (uint32_t shift = a.begin_bit; shift < a.end_bit; shift += B) {
+        const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
+        const uint32_t mask = (1u << width) - 1u;
+        if (shift != a.begin_bit) {
+            // this pass reads the previous pass's order, wave-striped
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t p = wbase + j * kWave + lane;
+                key[j] = s_key[cur][p];
+                if constexpr (PK != kResNone) val[j] = s_val[cur][p];
+            }
+        }
+        for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
+        __syncthreads();
+
+        uint32_t rank[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t p = wbase + j * kWave + lane;
+            const uint32_t d = (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip) >> shift) & mask) : (R - 1u);
+            const uint64_t m = match_mask<B>(d);
+            const uint32_t below = count_below(m);
+            const uint32_t before = s_cnt[wave][d];
+            rank[j] = (d << 16) | (before + below);
+            pin(rank[j]);
+            if (below == 0u) s_cnt[wave][d] = before + static_cast<uint32_t>(__popcll(m));
+        }
+        __syncthreads();
+
+        uint32_t count = 0u;
+        if (tid < static_cast<int>(R)) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const uint32_t c = s_cnt[w][tid];
+                s_cnt[w][tid] = count;
+                count += c;
+            }
+        }
+        const uint32_t start = block_exclusive_scan_n<BLOCK>(count, s_tmp, lane, wave);
+        if (tid < static_cast<int>(R)) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += start;
+        }
+        __syncthreads();
+
+        const int nxt = cur ^ 1;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t slot = s_cnt[wave][rank[j] >> 16] + (rank[j] & 0xFFFFu);
+            s_key[nxt][slot] = static_cast<Stored>(key[j]);
+            if constexpr (PK != kResNone) s_val[nxt][slot] = val[j];
+        }
+        cur = nxt;
+        __syncthreads();
+    }
+
+    // Write the sorted row; slots past the row end (padding) are dropped by
+    // the stores' range checks.
+    const __amdgpu_buffer_rsrc_t kout = make_rsrc(static_cast<Stored *>(a.keys_out) + row_base, n * sizeof(Stored));
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const uint32_t k = i * BLOCK + tid;
+        BufIO<Stored>::store(kout, k, s_key[cur][k]);
+    }
+    if constexpr (PK == kResU32) {
+        const __amdgpu_buffer_rsrc_t vout = make_rsrc(static_cast<uint32_t *>(a.vals_out) + row_base, n * 4u);
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const uint32_t k = i * BLOCK + tid;
+            BufIO<uint32_t>::store(vout, k, s_val[cur][k]);
+        }
+    } else if constexpr (PK == kResIndex) {
+        const __amdgpu_buffer_rsrc_t vout = make_rsrc(static_cast<int64_t *>(a.vals_out) + row_base, n * 8u);
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const uint32_t k = i * BLOCK + tid;
+            BufIO<int64_t>::store(vout, k, s_val[cur][k]);
+        }
+    }
+}
+
 // ------------------------------------------------------- digit histograms
 
 struct HistArgs {

@@ -48,6 +48,11 @@ def test_workspace_sizes():
     assert s4 >= 1024 * 65536 * (2 + 4 + 4) and s8 >= 1024 * 65536 * (2 + 4) and s4 > s8
     assert lib.segmented_row_sort_workspace_size(4, 1 << 30, 8) == 0
     assert lib.segmented_row_sort_workspace_size(0, 16, 8) == 0
+    # rows of at most 8192 elements are sorted whole in one workgroup: no workspace
+    assert lib.radix_sort_workspace_size(8192, 0, 32, 8, 1) == 0
+    assert lib.radix_sort_workspace_size(8193, 0, 32, 8, 1) > 0
+    assert lib.segmented_row_sort_workspace_size(4096, 4096, 8) == 0
+    assert lib.segmented_row_sort_workspace_size(4, 8193, 8) > 0
 
 
 def _gpu_present():
@@ -74,8 +79,9 @@ def test_validation_before_launch():
     assert st(k_in, k_out, 100, 8, 8, 8, ws, big, None) == 2
     assert st(k_in, k_out, 1 << 32, 0, 32, 8, ws, big, None) == 4
     assert st(None, k_out, 100, 0, 32, 8, ws, big, None) == 1
-    assert st(k_in, k_out, 100, 0, 32, 8, None, big, None) == 1
-    assert st(k_in, k_out, 100, 0, 32, 8, ws, 16, None) == 6
+    # inputs above 8192 elements need a workspace (smaller ones are sorted in one workgroup)
+    assert st(k_in, k_out, 100_000, 0, 32, 8, None, big, None) == 1
+    assert st(k_in, k_out, 100_000, 0, 32, 8, ws, 16, None) == 6
     assert st(k_in, k_in, 100, 0, 32, 8, ws, big, None) == 5
     assert st(k_in, ctypes.c_void_p(0x10000 + 200), 100, 0, 32, 8, ws, big, None) == 5
     assert st(None, None, 0, 0, 32, 8, None, 0, None) == 0  # n == 0: nothing to do
@@ -91,7 +97,7 @@ def test_validation_before_launch():
     assert seg(k_in, k_out, v_out, 4, 1 << 30, 0, 0, 8, ws, big, None) == 4
     assert seg(k_in, k_out, v_out, -1, 100, 0, 0, 8, ws, big, None) == 4
     assert seg(k_in, k_out, None, 4, 100, 0, 0, 8, ws, big, None) == 1
-    assert seg(k_in, k_out, v_out, 4, 100, 0, 0, 8, ws, 8, None) == 6
+    assert seg(k_in, k_out, v_out, 4, 100_000, 0, 0, 8, ws, 8, None) == 6
     assert seg(k_in, k_in, v_out, 4, 100, 0, 0, 8, ws, big, None) == 5
     assert seg(None, None, None, 0, 100, 0, 0, 8, None, 0, None) == 0
     h = lib.radix_sort_digit_histograms

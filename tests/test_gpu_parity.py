@@ -130,7 +130,7 @@ def test_pass_by_pass_states():
 
 def test_fuzz_sizes_windows_widths():
     rng = np.random.default_rng(2024)
-    sizes = [1, 2, 63, 64, 65, 255, 4095, 4096, 4097, 8191, 8193, 12289, 65537, 100_003]
+    sizes = [1, 2, 63, 64, 65, 255, 4095, 4096, 4097, 8191, 8192, 8193, 12289, 65537, 100_003]
     for trial, n in enumerate(sizes + [int(x) for x in rng.integers(1, 200_000, 10)]):
         keys = workloads.random_u32(700 + trial, n)
         if trial % 2:
@@ -186,7 +186,7 @@ def test_digit_histograms():
 
 
 def test_validation_with_real_buffers():
-    n = 4096
+    n = 100_000
     k = torch.zeros(n, dtype=torch.int32, device="cuda")
     o = torch.empty_like(k)
     with pytest.raises(ValueError):
@@ -270,8 +270,8 @@ def test_c5_bf16_4096x4096_descending():
     assert_same(gi.ravel(), ei.ravel(), "c5 indices")
 
 
-@pytest.mark.parametrize("rows,n", [(1, 1), (3, 7), (5, 4095), (2, 4097), (7, 12345), (1, 70000),
-                                     (300, 33), (2, 200_000)])
+@pytest.mark.parametrize("rows,n", [(1, 1), (3, 7), (5, 4095), (2, 4097), (3, 8192), (3, 8193), (7, 12345),
+                                     (1, 70000), (300, 33), (2, 200_000)])
 @pytest.mark.parametrize("b", [1, 2, 4, 8])
 def test_rows_ragged_shapes(rows, n, b):
     bits = workloads.fp16_normal_bits(rows * 131 + n, rows * n).reshape(rows, n)
