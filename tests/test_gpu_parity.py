@@ -285,3 +285,48 @@ def test_rows_ragged_shapes(rows, n, b):
             gv, gi = gpu_rows(bits, dtype, desc, b)
             assert_same(gv.ravel(), ev.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype}")
             assert_same(gi.ravel(), ei.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype} idx")
+
+
+# ------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("n", [1000, 300_000])
+def test_hip_graph_capture_and_replay(n):
+    """The whole sort (one resident launch, or clear + histogram + sweeps) is
+    captured once into a graph and replayed on new inputs copied into the
+    captured input buffers; every replay must equal the oracle and eager."""
+    kin = torch.empty(n, dtype=torch.int32, device="cuda")
+    vin = torch.empty_like(kin)
+    kout = torch.empty_like(kin)
+    vout = torch.empty_like(kin)
+    ws = torch.empty(max(1, lrs.radix_sort_workspace_size(n, 0, 32, 8, True)), dtype=torch.uint8, device="cuda")
+    first = workloads.random_u32(8800, n)
+    kin.copy_(to_gpu(first))
+    vin.copy_(to_gpu(np.arange(n, dtype=np.uint32)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        lrs.radix_sort_pairs(kin, vin, 0, 32, 8, keys_out=kout, values_out=vout, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lrs.radix_sort_pairs(kin, vin, 0, 32, 8, keys_out=kout, values_out=vout, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        keys = workloads.random_u32(8801 + rep, n)
+        if rep == 1:
+            keys &= workloads.random_u32(8900, n) & workloads.random_u32(8901, n)
+        vals = workloads.random_u32(8950 + rep, n)
+        kin.copy_(to_gpu(keys))
+        vin.copy_(to_gpu(vals))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
+        assert_same(to_np_u32(kout), ek, f"replay {rep} keys")
+        assert_same(to_np_u32(vout), ev, f"replay {rep} values")
+        # eager call between replays, same buffers
+        ko2, vo2 = lrs.radix_sort_pairs(kin, vin, 0, 32, 8)
+        torch.cuda.synchronize()
+        assert_same(to_np_u32(ko2), ek, f"eager {rep} keys")
+        assert_same(to_np_u32(vo2), ev, f"eager {rep} values")
