@@ -84,28 +84,38 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
+// Cache-policy bits of the streaming loads and stores (gfx940+: 1 = sc0,
+// 2 = nt, 16 = sc1); 0 = default caching.
+#ifndef LRS_LOAD_POLICY
+#define LRS_LOAD_POLICY 0
+#endif
+#ifndef LRS_STORE_POLICY
+#define LRS_STORE_POLICY 0
+#endif
+
 template <typename T> struct BufIO;
 template <> struct BufIO<uint32_t> {
     __device__ static inline uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t i) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(i * 4u), 0, 0);
+        return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(i * 4u), 0, LRS_LOAD_POLICY);
     }
     __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(i * 4u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(i * 4u), 0, LRS_STORE_POLICY);
     }
 };
 template <> struct BufIO<uint16_t> {
     __device__ static inline uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t i) {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(i * 2u), 0, 0);
+        return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(i * 2u), 0, LRS_LOAD_POLICY);
     }
     __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(i * 2u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(i * 2u), 0,
+                                              LRS_STORE_POLICY);
     }
 };
 template <> struct BufIO<int64_t> {
     typedef unsigned int v2u __attribute__((ext_vector_type(2)));
     __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
         const v2u w = {v, 0u};
-        __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(i * 8u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(i * 8u), 0, LRS_STORE_POLICY);
     }
 };
 
