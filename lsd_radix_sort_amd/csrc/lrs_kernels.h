@@ -125,25 +125,40 @@ __device__ inline void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
 
 // --------------------------------------------------------- wave utilities
 
-// Lanes of this wave whose digit equals this lane's digit (all 64 lanes must
-// be active): the AND, over the digit's B bits, of each bit's ballot or its
-// complement.
+// Lanes of this wave whose digit differs from this lane's digit (all 64 lanes
+// must be active).  For each of the digit's B bits the ballot gives the lanes
+// with the bit set; XOR with this lane's bit spread to all 32 bits (0 or ~0)
+// leaves the lanes that differ in that bit, and the mismatch mask is the OR of
+// those over all bits.  v_bitop3 does XOR and OR in one instruction: with
+// operands (spread, acc, ballot) the table 0xDE is acc | (spread ^ ballot).
 template <int B>
-__device__ inline uint64_t match_mask(uint32_t d) {
-    uint64_t m = ~0ull;
+__device__ inline uint64_t mismatch_mask(uint32_t d) {
+    uint32_t lo = 0u, hi = 0u;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-        const bool bit = (d >> i) & 1u;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
-        m &= bit ? bal : ~bal;
+        const uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), i, 1));
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(spread != 0u);
+        lo = __builtin_amdgcn_bitop3_b32(spread, lo, static_cast<uint32_t>(bal), 0xDE);
+        hi = __builtin_amdgcn_bitop3_b32(spread, hi, static_cast<uint32_t>(bal >> 32), 0xDE);
     }
-    return m;
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // Number of set bits of m at lanes below this lane.
 __device__ inline uint32_t count_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// This lane's rank among the lanes of its digit group, and the group's size,
+// from the group's member mask (LDS matching) or its mismatch mask (ballots).
+__device__ inline void group_rank_from_members(uint64_t members, uint32_t &below, uint32_t &size) {
+    below = count_below(members);
+    size = static_cast<uint32_t>(__popcll(members));
+}
+__device__ inline void group_rank_from_mismatch(uint64_t mismatch, int lane, uint32_t &below, uint32_t &size) {
+    below = static_cast<uint32_t>(lane) - count_below(mismatch);
+    size = 64u - static_cast<uint32_t>(__popcll(mismatch));
 }
 
 __device__ inline uint32_t wave_inclusive_scan(uint32_t x, int lane) {
@@ -295,19 +310,18 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
         const uint32_t p = wbase + j * kWave + lane;
         const uint32_t d = (p < valid)
             ? ((KeyTraits<KK>::key(key[j], a.flip) >> a.shift) & a.digit_mask) : (R - 1u);
-        uint64_t m;
+        uint32_t below, size;
         if constexpr (MATCH == kMatchBallot) {
-            m = match_mask<B>(d);
+            group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
         } else {
             atomicOr(&s_match[wave][d], static_cast<unsigned long long>(lane_bit));
-            m = s_match[wave][d];
+            group_rank_from_members(s_match[wave][d], below, size);
         }
-        const uint32_t below = count_below(m);
         const uint32_t before = s_cnt[wave][d];
         rank[j] = (d << 16) | (before + below);
         pin(rank[j]);
         if (below == 0u) {
-            s_cnt[wave][d] = before + static_cast<uint32_t>(__popcll(m));
+            s_cnt[wave][d] = before + size;
             if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
         }
     }
@@ -535,12 +549,12 @@ __global__ __launch_bounds__(BLOCK) void resident_sort_kernel(ResidentArgs a) {
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t p = wbase + j * kWave + lane;
             const uint32_t d = (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip) >> shift) & mask) : (R - 1u);
-            const uint64_t m = match_mask<B>(d);
-            const uint32_t below = count_below(m);
+            uint32_t below, size;
+            group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
             const uint32_t before = s_cnt[wave][d];
             rank[j] = (d << 16) | (before + below);
             pin(rank[j]);
-            if (below == 0u) s_cnt[wave][d] = before + static_cast<uint32_t>(__popcll(m));
+            if (below == 0u) s_cnt[wave][d] = before + size;
         }
         __syncthreads();
 
