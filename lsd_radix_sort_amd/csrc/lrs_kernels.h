@@ -27,7 +27,7 @@ namespace lrs {
 
 // Compile-time tunables (defaults are the measured choices).
 #ifndef LRS_SWEEP_ITEMS
-#define LRS_SWEEP_ITEMS 24      // keys per thread in the largest sweep tile
+#define LRS_SWEEP_ITEMS 28      // keys per thread in the largest sweep tile
 #endif
 #ifndef LRS_SWEEP_BLOCK
 #define LRS_SWEEP_BLOCK 512     // threads per workgroup of the largest sweep tile

@@ -99,8 +99,8 @@ def test_c3_pairs_reduced_size(dist):
 
 @pytest.mark.parametrize("b,dist", [(8, "uniform"), (4, "and3")])
 def test_large_tile_configuration(b, dist):
-    # enough elements for the largest sweep tile (at least 1024 tiles of 12288)
-    n = 13_000_003
+    # enough elements for the largest sweep tile (at least 1024 tiles of 14336)
+    n = 15_000_007
     keys = workloads.random_u32(4000 + b, n)
     if dist == "and3":
         keys &= workloads.random_u32(4100, n) & workloads.random_u32(4200, n)
