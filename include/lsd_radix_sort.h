@@ -136,6 +136,18 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
 int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
 
 /*
+ * Bound on how long a sweep tile waits for the counts an earlier tile of its
+ * row publishes (decoupled look-back), in polls of about a microsecond each.
+ * When a tile runs out of polls it counts its digit over the keys of the
+ * earlier tiles of its row instead, which gives the same result; the bound
+ * only guarantees that no launch waits forever, whatever order the hardware
+ * starts workgroups in.  0 makes every tile count from the keys (slow; it
+ * exists to test that path).  The default is 65536.  Applies to sorts enqueued
+ * after the call; returns the previous value.  Not thread-safe.
+ */
+uint32_t radix_sort_set_spin_limit(uint32_t polls);
+
+/*
  * Kernel timing for measurement.  After radix_sort_timing_begin(), every
  * kernel the library enqueues is bracketed by HIP events on its stream.
  * radix_sort_timing_end() waits for those events and reports, per kernel kind

@@ -71,6 +71,8 @@ def load_library():
     lib.radix_sort_digit_histograms.restype = c_int
     lib.radix_sort_copy_probe.argtypes = [P, P, szt, P]
     lib.radix_sort_copy_probe.restype = c_int
+    lib.radix_sort_set_spin_limit.argtypes = [ctypes.c_uint32]
+    lib.radix_sort_set_spin_limit.restype = ctypes.c_uint32
     lib.radix_sort_timing_begin.argtypes = []
     lib.radix_sort_timing_begin.restype = c_int
     lib.radix_sort_timing_end.argtypes = [P, P]
@@ -206,6 +208,17 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst smaller than src")
     _check(lib.radix_sort_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src)), "copy_probe")
+
+
+def radix_sort_set_spin_limit(polls: int) -> int:
+    """Bound, in polls, on a sweep tile's wait for an earlier tile's counts.
+
+    Past it the tile counts its prefix from the keys (same result); 0 makes
+    every tile do so.  Returns the previous bound.
+    """
+    if not 0 <= polls <= 0xFFFFFFFF:
+        raise ValueError("polls must fit in 32 bits")
+    return int(load_library().radix_sort_set_spin_limit(polls))
 
 
 class KernelTimer:

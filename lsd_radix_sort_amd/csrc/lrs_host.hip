@@ -46,7 +46,12 @@ int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
     return 0;
 }
 constexpr uint64_t kAlign = 256;
-constexpr uint32_t kHistTargetBlocks = 2048;
+#ifndef LRS_HIST_BLOCKS
+#define LRS_HIST_BLOCKS 2048
+#endif
+// Histogram workgroups per launch (measured on 2^28 keys: 2048 spans beat
+// 640, 1280, 2560 and 5120, and beat interleaved strips).
+constexpr uint32_t kHistTargetBlocks = LRS_HIST_BLOCKS;
 constexpr uint32_t kHistMinChunk = 4096;
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -90,6 +95,12 @@ struct TimedLaunch {
     }
 };
 
+// Polls of an unpublished look-back word before a tile counts its prefix from
+// the keys (about 1 us each, so the default is tens of milliseconds: far beyond
+// any wait of a running sort, and only a guarantee against waiting forever).
+constexpr uint32_t kDefaultSpinLimit = 1u << 16;
+uint32_t g_spin_limit = kDefaultSpinLimit;
+
 // ------------------------------------------------------------ planning
 
 struct Plan {
@@ -104,7 +115,6 @@ struct Plan {
     uint32_t tiles_per_row = 0;
     uint64_t num_tiles = 0;
     bool wide_status = false;       // 64-bit look-back words, 64-bit stores (row_len >= 2^29)
-    uint32_t hist_chunk = 0;
     uint32_t hist_chunks_per_row = 0;
     // workspace layout (byte offsets)
     uint64_t off_hist = 0, hist_words = 0;
@@ -129,12 +139,10 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.num_tiles = rows * p.tiles_per_row;
     p.wide_status = row_len >= (1ull << 29);
 
-    // histogram chunking: about kHistTargetBlocks workgroups in all
-    uint64_t chunks = std::max<uint64_t>(1, std::min<uint64_t>(cdiv(row_len, kHistMinChunk),
-                                                                cdiv(kHistTargetBlocks, rows)));
-    uint64_t chunk = align_up(cdiv(row_len, chunks), 1024);
-    p.hist_chunk = static_cast<uint32_t>(std::min<uint64_t>(chunk, 0x80000000ull));
-    p.hist_chunks_per_row = static_cast<uint32_t>(cdiv(row_len, p.hist_chunk));
+    // histogram: about kHistTargetBlocks workgroups in all, at least
+    // kHistMinChunk keys each
+    p.hist_chunks_per_row = static_cast<uint32_t>(std::max<uint64_t>(
+        1, std::min<uint64_t>(cdiv(row_len, kHistMinChunk), cdiv(kHistTargetBlocks, rows))));
 
     const uint64_t keysz = (kind == 2) ? 2 : 4;
     const uint64_t n = rows * row_len;
@@ -143,7 +151,7 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.hist_words = rows * p.passes * R;
     off = align_up(off + 4 * p.hist_words, kAlign);
     p.off_counters = off;
-    p.counter_words = static_cast<uint64_t>(p.passes);
+    p.counter_words = static_cast<uint64_t>(p.passes) * kXcds;
     off = align_up(off + 4 * p.counter_words, kAlign);
     p.status_bytes = p.num_tiles * R * (p.wide_status ? 8 : 4);
     const int status_bufs = p.passes > 1 ? 2 : 1;
@@ -302,7 +310,6 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     h.hist = hist;
     h.row_len = static_cast<uint32_t>(p.row_len);
     h.chunks_per_row = p.hist_chunks_per_row;
-    h.chunk = p.hist_chunk;
     h.passes = static_cast<uint32_t>(p.passes);
     h.begin_bit = static_cast<uint32_t>(p.begin_bit);
     h.end_bit = static_cast<uint32_t>(p.end_bit);
@@ -323,7 +330,7 @@ SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass) {
     a.hist_row_stride = static_cast<uint32_t>(p.passes * R);
     a.status = ws + p.off_status[pass & 1];
     a.status_next = (pass + 1 < p.passes) ? ws + p.off_status[(pass + 1) & 1] : nullptr;
-    a.tile_counter = reinterpret_cast<uint32_t *>(ws + p.off_counters) + pass;
+    a.tile_counter = reinterpret_cast<uint32_t *>(ws + p.off_counters) + static_cast<uint64_t>(pass) * kXcds;
     a.row_len = static_cast<uint32_t>(p.row_len);
     a.tiles_per_row = p.tiles_per_row;
     a.num_tiles = static_cast<uint32_t>(p.num_tiles);
@@ -332,6 +339,7 @@ SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass) {
     a.shift = static_cast<uint32_t>(shift);
     a.digit_mask = (1u << width) - 1u;
     a.flip = 0;
+    a.spin_limit = g_spin_limit;
     return a;
 }
 
@@ -551,7 +559,7 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint64_t n16 = bytes / 16;
     const uint32_t tail = static_cast<uint32_t>(bytes % 16);
-    const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(8192, std::max<uint64_t>(1, cdiv(n16, kBlock * 4))));
+    const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(1u << 20, std::max<uint64_t>(1, cdiv(n16, kBlock))));
     TimedLaunch t(3, s);
     copy_kernel<<<blocks, kBlock, 0, s>>>(static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16,
                                           static_cast<const uint8_t *>(src) + n16 * 16,
@@ -559,6 +567,12 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
     hipError_t e = hipGetLastError();
     t.done();
     return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
+uint32_t radix_sort_set_spin_limit(uint32_t polls) {
+    const uint32_t old = g_spin_limit;
+    g_spin_limit = polls;
+    return old;
 }
 
 int radix_sort_timing_begin(void) {

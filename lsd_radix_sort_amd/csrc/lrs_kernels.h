@@ -38,10 +38,15 @@ namespace lrs {
 #ifndef LRS_HIST_COPIES
 #define LRS_HIST_COPIES 8       // LDS copies of the histogram, lanes spread over them
 #endif
+#ifndef LRS_XCD_CHUNK
+#define LRS_XCD_CHUNK 16        // consecutive sweep tiles handed to one XCD at a time
+#endif
 
 constexpr int kBlock = 256;            // threads per workgroup (histogram, utilities)
 constexpr int kSweepBlock = LRS_SWEEP_BLOCK;
 constexpr int kLookback = LRS_LOOKBACK;
+constexpr uint32_t kXcdChunk = LRS_XCD_CHUNK;
+constexpr uint32_t kXcds = 8;          // accelerator complex dies (XCDs) of an MI355X
 constexpr int kWave = 64;              // CDNA wavefront width
 
 enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1 };
@@ -202,7 +207,7 @@ struct SweepArgs {
     const uint32_t *hist;    // this pass's digit counts of row 0; row r at hist + r * hist_row_stride
     void *status;            // [num_tiles][R] look-back words of this pass
     void *status_next;       // the next pass's words, cleared here (NULL on the last pass)
-    uint32_t *tile_counter;  // this pass's tile ticket counter, zero on entry
+    uint32_t *tile_counter;  // this pass's kXcds tile ticket counters, zero on entry
     uint32_t row_len;        // elements per row
     uint32_t tiles_per_row;
     uint32_t num_tiles;      // rows * tiles_per_row = grid size
@@ -210,7 +215,30 @@ struct SweepArgs {
     uint32_t shift;          // lowest bit of this pass's digit
     uint32_t digit_mask;     // (1 << width) - 1
     uint32_t flip;           // 0xFFFF for descending 16-bit float keys, else 0
+    uint32_t spin_limit;     // polls of an unpublished look-back word before the tile counts
+                             // its prefix from the keys; 0: always count from the keys
 };
+
+// Tile handed to the calling workgroup.  The tiles of a pass are dealt to the
+// XCDs in chunks of kXcdChunk consecutive tiles (chunk c to XCD c % kXcds), and
+// each XCD hands out its own chunks in order from its own counter; a workgroup
+// whose XCD has none left takes one from the next XCD's counter.  Neighbouring
+// tiles then mostly run on one XCD at the same time, so the cache lines that
+// their digit runs share are merged in that XCD's L2 instead of being written
+// back partially by two XCDs.  With one workgroup per tile every tile is taken
+// exactly once (a workgroup that found all counters exhausted would mean that
+// the other workgroups took every tile).  Returns num_tiles only if the grid
+// has more workgroups than tiles.
+__device__ inline uint32_t take_tile(uint32_t *counters, uint32_t num_tiles) {
+    const uint32_t xcd = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % kXcds;  // XCC_ID
+    for (uint32_t i = 0; i < kXcds; ++i) {
+        const uint32_t x = (xcd + i) % kXcds;
+        const uint32_t k = atomicAdd(counters + x, 1u);
+        const uint64_t tile = (static_cast<uint64_t>(k / kXcdChunk) * kXcds + x) * kXcdChunk + k % kXcdChunk;
+        if (tile < num_tiles) return static_cast<uint32_t>(tile);
+    }
+    return num_tiles;
+}
 
 // How a wave finds the lanes that share its digit.
 enum MatchKind : int { kMatchBallot = 0, kMatchLds = 1 };
@@ -244,7 +272,8 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
 //    each wave's base inside it, and the row's bucket base.
 // 4. Move every key to its slot of the tile's digit order in LDS, then walk
 //    the look-back: the digit's count in earlier tiles of the row, read from
-//    the predecessors' published words until an inclusive count is met.
+//    the predecessors' published words until an inclusive count is met (or,
+//    after a bounded wait, counted from the earlier tiles' keys).
 // 5. Publish this tile's inclusive counts, then write the keys (and then the
 //    payload through the same slots) with consecutive threads taking
 //    consecutive slots, so each digit run goes to consecutive addresses.
@@ -266,6 +295,7 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     __shared__ uint8_t s_dig[PK != kPayNone ? TILE : 1];  // digit of each slot, for the payload
     __shared__ uint32_t s_tmp[WAVES];
     __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_gave_up;            // a look-back wave stopped waiting
     auto s_match = reinterpret_cast<unsigned long long (*)[R]>(s_buf);
 
     const int tid = threadIdx.x;
@@ -277,13 +307,16 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
     if constexpr (MATCH == kMatchLds)
         for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_match[0][0])[i] = 0ull;
-    if (tid == 0) s_ticket = atomicAdd(a.tile_counter, 1u);
+    if (tid == 0) {
+        s_ticket = take_tile(a.tile_counter, a.num_tiles);
+        s_gave_up = 0u;
+    }
     __syncthreads();
 
-    // Tiles are handed out in ticket order, so every tile this one waits for
-    // below is already running.  Tiles are numbered row-major.
+    // Tiles are numbered row-major.  A tile waits below only for earlier tiles
+    // of its row, and for a bounded number of polls (see the look-back).
     const uint32_t t = s_ticket;
-    if (t >= a.num_tiles) return;  // cannot happen with a zeroed counter and grid == num_tiles
+    if (t >= a.num_tiles) return;  // cannot happen with zeroed counters and grid == num_tiles
     const uint32_t row = t / a.tiles_per_row;
     const uint32_t tile_in_row = t - row * a.tiles_per_row;
     const uint32_t tile_start = tile_in_row * TILE;
@@ -379,14 +412,22 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     // lane polls a single word (with a short sleep) until the predecessor has
     // published, instead of all of them re-reading memory.  The row's first
     // tile publishes an inclusive count at once, so no walk leaves the row.
+    //
+    // Waiting is bounded: after spin_limit polls the wave gives up, and the
+    // workgroup counts the digit over the row's keys before this tile instead
+    // (the exact exclusive prefix, at the cost of reading them).  So no tile
+    // waits forever, whatever order the hardware starts workgroups in.
     {
         W excl = 0;
-        bool done = tile_in_row == 0 || tid >= static_cast<int>(R);
+        const bool from_keys = a.spin_limit == 0u && tile_in_row != 0u;
+        bool done = tile_in_row == 0 || from_keys || tid >= static_cast<int>(R);
+        bool gave_up = false;  // uniform in the wave
+        uint32_t polls = 0;
         uint32_t back = 1;  // the next predecessor to consume is tile t - back
         const W *row_status = static_cast<const W *>(a.status) + tid;
         for (;;) {
             const uint64_t walking = __builtin_amdgcn_ballot_w64(!done);
-            if (walking == 0) break;
+            if (walking == 0 || gave_up) break;
             W sv[kLookback];
 #pragma unroll
             for (int i = 0; i < kLookback; ++i)
@@ -406,12 +447,30 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
                 const int leader = __builtin_ctzll(walking);
                 const W *word = row_status + static_cast<uint64_t>(t - back) * R;
                 for (;;) {
+                    if (++polls > a.spin_limit) {
+                        gave_up = true;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
                     W pv = 0;
                     if (lane == leader) pv = observe(word);
                     if (__builtin_amdgcn_ballot_w64(lane == leader && (pv & ~St::kMask) != 0) != 0) break;
                 }
             }
+        }
+        if (gave_up && lane == 0) s_gave_up = 1u;
+        __syncthreads();
+        if (from_keys || s_gave_up != 0u) {
+            if (tid < static_cast<int>(R)) s_goff[tid] = 0u;
+            __syncthreads();
+            const Stored *row_keys = static_cast<const Stored *>(a.keys_in) + row_base;
+            for (uint32_t i = tid; i < tile_start; i += BLOCK) {
+                const uint32_t d = (KeyTraits<KK>::key(row_keys[i], a.flip) >> a.shift) & a.digit_mask;
+                atomicAdd(&s_goff[d], 1u);
+            }
+            __syncthreads();
+            if (tid < static_cast<int>(R)) excl = s_goff[tid];
+            __syncthreads();
         }
         if (tid < static_cast<int>(R)) {
             if (tile_in_row != 0)
@@ -616,8 +675,7 @@ struct HistArgs {
     const void *keys;
     uint32_t *hist;          // [rows][passes][R], zero on entry when atomic != 0
     uint32_t row_len;
-    uint32_t chunks_per_row;
-    uint32_t chunk;          // elements per workgroup, a multiple of 8
+    uint32_t chunks_per_row; // workgroups per row
     uint32_t passes;
     uint32_t begin_bit;
     uint32_t end_bit;
@@ -627,17 +685,25 @@ struct HistArgs {
 
 constexpr int kHistMaxCounters = 1024;  // passes * R for every legal (window, b)
 constexpr int kHistCopies = LRS_HIST_COPIES;
+#ifndef LRS_HIST_INTERLEAVE
+#define LRS_HIST_INTERLEAVE 0   // 0: one span of the row per workgroup; 1: 4 KiB strips in turn
+#endif
 
-// Counts every pass's digit over one chunk of one row in LDS, from one read of
+// Counts every pass's digit over one share of one row in LDS, from one read of
 // the keys with 16-byte loads, then adds the counts to the row's histogram.
 // Lane l counts into copy l % kHistCopies of the counters (copies of one
 // counter sit in consecutive words), so lanes that share a digit mostly hit
-// different LDS banks instead of serialising on one address.
+// different LDS banks instead of serialising on one address.  The pass loop
+// is unrolled: each pass costs one bit-field extract, one address add and one
+// LDS add whose pass offset is an immediate.
 template <int B, int KK>
 __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t R = 1u << B;
     using Stored = typename KeyTraits<KK>::Stored;
     constexpr uint32_t kPerVec = 16u / sizeof(Stored);
+    constexpr int kMaxPasses = (8 * static_cast<int>(sizeof(Stored)) + B - 1) / B;
+    constexpr uint32_t kPassWords = R * kHistCopies;
+    static_assert(kMaxPasses * R <= kHistMaxCounters, "counters must fit");
     constexpr int kUnroll = 4;
     __shared__ uint32_t s_h[kHistMaxCounters * kHistCopies];
 
@@ -647,18 +713,17 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     for (uint32_t i = threadIdx.x; i < total * kHistCopies; i += kBlock) s_h[i] = 0u;
     __syncthreads();
 
-    const uint32_t lo = chunk * a.chunk;
-    const uint32_t hi = min(a.row_len, lo + a.chunk);
-    const Stored *base = static_cast<const Stored *>(a.keys) + static_cast<uint64_t>(row) * a.row_len;
     uint32_t *mine = s_h + (threadIdx.x % kHistCopies);
-
     auto count_key = [&](uint32_t v) {
         const uint32_t k = KeyTraits<KK>::key(v, a.flip);
-        for (uint32_t p = 0; p < a.passes; ++p) {
-            const uint32_t shift = a.begin_bit + p * B;
-            const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
-            const uint32_t d = (k >> shift) & ((1u << width) - 1u);
-            atomicAdd(mine + (p * R + d) * kHistCopies, 1u);
+#pragma unroll
+        for (int p = 0; p < kMaxPasses; ++p) {
+            if (p < static_cast<int>(a.passes)) {
+                const uint32_t shift = a.begin_bit + static_cast<uint32_t>(p) * B;
+                const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
+                const uint32_t d = __builtin_amdgcn_ubfe(k, shift, width);
+                atomicAdd(mine + p * kPassWords + d * kHistCopies, 1u);
+            }
         }
     };
     auto count_vec = [&](const uint4 &w) {
@@ -672,36 +737,48 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
         }
     };
 
-    // 16-byte loads when the chunk starts 16-byte aligned; lo is a multiple of
-    // the chunk size (a multiple of 8), so only the row start can misalign it.
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + lo);
-    uint32_t i = lo;
-    if ((addr & 15u) == 0u) {
-        const uint32_t nvec = (hi - lo) / kPerVec;
-        const uint4 *v4 = reinterpret_cast<const uint4 *>(base + lo);
-        uint32_t q = threadIdx.x;
-        for (; q + (kUnroll - 1) * kBlock < nvec; q += kUnroll * kBlock) {
-            uint4 w[kUnroll];
+    // The row splits into a head up to the first 16-byte boundary, whole
+    // 16-byte words, and a tail; rows start on an element boundary.
+    const Stored *base = static_cast<const Stored *>(a.keys) + static_cast<uint64_t>(row) * a.row_len;
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & 15u) / sizeof(Stored);
+    const uint32_t head = min(a.row_len, mis != 0u ? kPerVec - mis : 0u);
+    const uint32_t nvec = (a.row_len - head) / kPerVec;
+    const uint32_t body_end = head + nvec * kPerVec;
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(base + head);
+
+#if LRS_HIST_INTERLEAVE
+    const uint32_t step = a.chunks_per_row * kBlock;
+    uint32_t q = chunk * kBlock + threadIdx.x;
+    const uint32_t q_end = nvec;
+#else
+    const uint32_t per = (nvec + a.chunks_per_row - 1) / a.chunks_per_row;
+    const uint32_t step = kBlock;
+    uint32_t q = chunk * per + threadIdx.x;
+    const uint32_t q_end = min(nvec, chunk * per + per);
+#endif
+    for (; q + (kUnroll - 1) * step < q_end; q += kUnroll * step) {
+        uint4 w[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) w[u] = v4[q + u * kBlock];
+        for (int u = 0; u < kUnroll; ++u) w[u] = v4[q + u * step];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) count_vec(w[u]);
-        }
-        for (; q < nvec; q += kBlock) count_vec(v4[q]);
-        i = lo + nvec * kPerVec;
+        for (int u = 0; u < kUnroll; ++u) count_vec(w[u]);
     }
-    for (uint32_t q = i + threadIdx.x; q < hi; q += kBlock) count_key(static_cast<uint32_t>(base[q]));
+    for (; q < q_end; q += step) count_vec(v4[q]);
+    if (chunk == 0 && threadIdx.x < head) count_key(static_cast<uint32_t>(base[threadIdx.x]));
+    if (chunk == a.chunks_per_row - 1 && body_end + threadIdx.x < a.row_len)
+        count_key(static_cast<uint32_t>(base[body_end + threadIdx.x]));
     __syncthreads();
 
     uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
-    for (uint32_t q = threadIdx.x; q < total; q += kBlock) {
+    for (uint32_t i = threadIdx.x; i < total; i += kBlock) {
+        const uint32_t p = i / R, d = i - p * R;
         uint32_t c = 0;
 #pragma unroll
-        for (int k = 0; k < kHistCopies; ++k) c += s_h[q * kHistCopies + k];
+        for (int k = 0; k < kHistCopies; ++k) c += s_h[p * kPassWords + d * kHistCopies + k];
         if (a.atomic) {
-            if (c) atomicAdd(out + q, c);
+            if (c) atomicAdd(out + i, c);
         } else {
-            out[q] = c;
+            out[i] = c;
         }
     }
 }
@@ -729,21 +806,16 @@ __global__ __launch_bounds__(kBlock) void clear_kernel(ClearArgs a) {
     }
 }
 
-// Plain streaming copy, four 16-byte loads in flight per thread.
+// Plain streaming copy: one 16-byte word per thread and a grid that covers the
+// buffer once (a grid-stride loop only past 2^20 workgroups).  On MI355X this
+// shape moves about 6.1 TB/s; unrolled or grid-stride shapes with more bytes
+// per thread in flight lose a quarter of that or more.
 __global__ __launch_bounds__(kBlock) void copy_kernel(const uint4 *src, uint4 *dst, uint64_t n16,
                                                       const uint8_t *src_tail, uint8_t *dst_tail,
                                                       uint32_t tail) {
-    constexpr int kUnroll = 4;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x;
-    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-        uint4 w[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = src[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = w[u];
-    }
-    for (; i < n16; i += stride) dst[i] = src[i];
+    for (uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
     if (blockIdx.x == 0 && threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 

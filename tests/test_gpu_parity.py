@@ -287,6 +287,54 @@ def test_rows_ragged_shapes(rows, n, b):
             assert_same(gi.ravel(), ei.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype} idx")
 
 
+# ------------------------------------------------ bounded look-back waits
+
+@pytest.fixture
+def spin_limit():
+    old = lrs.radix_sort_set_spin_limit(0)
+    yield lrs.radix_sort_set_spin_limit
+    lrs.radix_sort_set_spin_limit(old)
+
+
+@pytest.mark.parametrize("limit", [0, 1])
+def test_prefix_counted_from_keys(limit, spin_limit):
+    """With the look-back wait bounded to `limit` polls (0: no look-back at
+    all), tiles count their prefix over the earlier tiles' keys; the sort must
+    not change."""
+    spin_limit(limit)
+    n = 300_001
+    keys = workloads.random_u32(9100, n) & workloads.random_u32(9101, n)
+    vals = np.arange(n, dtype=np.uint32)
+    for b, begin, end in ((8, 0, 32), (4, 3, 30), (1, 0, 5), (2, 7, 18)):
+        log(f"limit={limit} n={n} b={b} bits [{begin},{end})")
+        ek, ev = oracle.radix_sort_pairs(keys, vals, begin, end, b)
+        gk, gv = gpu_pairs(keys, vals, begin, end, b)
+        assert_same(gk, ek, "keys")
+        assert_same(gv, ev, "values")
+        assert_same(gpu_keys(keys, begin, end, b), ek, "keys only")
+    rows, m = 5, 20001
+    bits = workloads.fp16_normal_bits(9200, rows * m).reshape(rows, m)
+    for desc, dtype, b in ((False, "fp16", 4), (True, "bf16", 8)):
+        log(f"limit={limit} rows {rows}x{m} {dtype} desc={desc} b={b}")
+        ev, ei = oracle.segmented_row_sort(bits, desc, b)
+        gv, gi = gpu_rows(bits, dtype, desc, b)
+        assert_same(gv.ravel(), ev.ravel(), "row values")
+        assert_same(gi.ravel(), ei.ravel(), "row indices")
+
+
+def test_prefix_counted_from_keys_large_tiles(spin_limit):
+    # the largest tile shape, every tile counting its prefix from the keys
+    spin_limit(0)
+    n = 15_000_007
+    keys = workloads.random_u32(9300, n)
+    vals = np.arange(n, dtype=np.uint32)
+    log(f"limit=0 large tiles n={n}")
+    ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
+    gk, gv = gpu_pairs(keys, vals, 0, 32, 8)
+    assert_same(gk, ek, "keys")
+    assert_same(gv, ev, "values")
+
+
 # ------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("n", [1000, 300_000])
