@@ -36,12 +36,15 @@ constexpr uint64_t kMinTiles = 1024;  // about four tiles per CU
 // Rows up to this length are sorted whole inside one workgroup's LDS.
 constexpr uint64_t kResidentMax = 8192;
 
+// The largest tile shape with at least kMinTiles tiles and at most 1/32 of
+// its elements past row ends (rows of 65536 take 8192-key tiles, not five
+// 14336-key tiles with 8.6% padding).
 int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
     for (int c = 2; c >= 1; --c) {
         const uint64_t tile = kTileCfgs[c].tile;
         const uint64_t tiles = rows * ((row_len + tile - 1) / tile);
         const uint64_t padded = tiles * tile;
-        if (tiles >= kMinTiles && (padded - rows * row_len) * 10 <= padded) return c;
+        if (tiles >= kMinTiles && (padded - rows * row_len) * 32 <= padded) return c;
     }
     return 0;
 }

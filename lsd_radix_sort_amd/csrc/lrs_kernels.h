@@ -136,12 +136,15 @@ __device__ inline void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
 // leaves the lanes that differ in that bit, and the mismatch mask is the OR of
 // those over all bits.  v_bitop3 does XOR and OR in one instruction: with
 // operands (spread, acc, ballot) the table 0xDE is acc | (spread ^ ballot).
+// The ballot is taken from the spread itself (one compare); without the pin
+// the compiler derives it from d with a shift and a compare instead.
 template <int B>
 __device__ inline uint64_t mismatch_mask(uint32_t d) {
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-        const uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), i, 1));
+        uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), i, 1));
+        pin(spread);
         const uint64_t bal = __builtin_amdgcn_ballot_w64(spread != 0u);
         lo = __builtin_amdgcn_bitop3_b32(spread, lo, static_cast<uint32_t>(bal), 0xDE);
         hi = __builtin_amdgcn_bitop3_b32(spread, hi, static_cast<uint32_t>(bal >> 32), 0xDE);
@@ -338,26 +341,32 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     // running count (and clears the mask).
     const uint64_t lane_bit = 1ull << lane;
     uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's digit
+    // Only a row's last tile has elements past the end, so full tiles take a
+    // copy of the loop without the bounds test.
+    auto rank_items = [&](auto partial) {
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const uint32_t p = wbase + j * kWave + lane;
-        const uint32_t d = (p < valid)
-            ? ((KeyTraits<KK>::key(key[j], a.flip) >> a.shift) & a.digit_mask) : (R - 1u);
-        uint32_t below, size;
-        if constexpr (MATCH == kMatchBallot) {
-            group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
-        } else {
-            atomicOr(&s_match[wave][d], static_cast<unsigned long long>(lane_bit));
-            group_rank_from_members(s_match[wave][d], below, size);
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t p = wbase + j * kWave + lane;
+            const uint32_t dig = (KeyTraits<KK>::key(key[j], a.flip) >> a.shift) & a.digit_mask;
+            const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
+            uint32_t below, size;
+            if constexpr (MATCH == kMatchBallot) {
+                group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
+            } else {
+                atomicOr(&s_match[wave][d], static_cast<unsigned long long>(lane_bit));
+                group_rank_from_members(s_match[wave][d], below, size);
+            }
+            const uint32_t before = s_cnt[wave][d];
+            rank[j] = (d << 16) | (before + below);
+            pin(rank[j]);
+            if (below == 0u) {
+                s_cnt[wave][d] = before + size;
+                if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
+            }
         }
-        const uint32_t before = s_cnt[wave][d];
-        rank[j] = (d << 16) | (before + below);
-        pin(rank[j]);
-        if (below == 0u) {
-            s_cnt[wave][d] = before + size;
-            if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
-        }
-    }
+    };
+    if (valid == TILE) rank_items(std::false_type{});
+    else rank_items(std::true_type{});
     __syncthreads();
 
     // 3. Digit d is owned by thread d.
