@@ -32,7 +32,12 @@ struct TileCfg {
 };
 constexpr TileCfg kTileCfgs[3] = {
     {256, 16, 4096}, {512, 16, 8192}, {kSweepBlock, LRS_SWEEP_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_ITEMS}};
-constexpr uint64_t kMinTiles = 1024;  // about four tiles per CU
+#ifndef LRS_MIN_TILES
+#define LRS_MIN_TILES 256
+#endif
+// Fewest tiles a larger tile shape must still give: one per CU (4M keys take
+// 512 8192-key tiles, 22% faster per sort than 1024 4096-key tiles).
+constexpr uint64_t kMinTiles = LRS_MIN_TILES;
 // Rows up to this length are sorted whole inside one workgroup's LDS.
 constexpr uint64_t kResidentMax = 8192;
 
@@ -55,7 +60,13 @@ constexpr uint64_t kAlign = 256;
 // Histogram workgroups per launch (measured on 2^28 keys: 2048 spans beat
 // 640, 1280, 2560 and 5120, and beat interleaved strips).
 constexpr uint32_t kHistTargetBlocks = LRS_HIST_BLOCKS;
-constexpr uint32_t kHistMinChunk = 4096;
+#ifndef LRS_HIST_MIN_CHUNK
+#define LRS_HIST_MIN_CHUNK 16384
+#endif
+// Fewest keys per histogram workgroup: each workgroup adds its counters to the
+// row's histogram with global atomics, and on 4M keys 1024 workgroups spent
+// more time on those than on reading (26 us against 16 us with 256).
+constexpr uint32_t kHistMinChunk = LRS_HIST_MIN_CHUNK;
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }

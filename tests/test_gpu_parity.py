@@ -113,6 +113,22 @@ def test_large_tile_configuration(b, dist):
     assert_same(gpu_keys(keys, 0, 32, b), ek, "keys only")
 
 
+@pytest.mark.parametrize("b,dist", [(8, "and3"), (4, "uniform")])
+def test_mid_tile_configuration(b, dist):
+    # too few elements for 256 tiles of 14336, enough for 256 of 8192
+    n = 3_000_017
+    keys = workloads.random_u32(4300 + b, n)
+    if dist == "and3":
+        keys &= workloads.random_u32(4400, n) & workloads.random_u32(4500, n)
+    vals = np.arange(n, dtype=np.uint32)
+    log(f"mid tiles n={n} b={b} {dist}")
+    ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, b)
+    gk, gv = gpu_pairs(keys, vals, 0, 32, b)
+    assert_same(gk, ek, "keys")
+    assert_same(gv, ev, "values")
+    assert_same(gpu_keys(keys, 0, 32, b), ek, "keys only")
+
+
 def test_pass_by_pass_states():
     # the state after p passes is the stable sort by the low p*b bits of the window
     n = 300_001
