@@ -66,6 +66,11 @@ WORKLOADS = {
     "c5_bf16_4096x4096_desc": dict(kind="rows", rows=4096, cols=4096, dtype="bf16", descending=True, b=8,
                                    desc="bf16 (4096, 4096) 64-level N(0,1) rows, descending, int64 column index, "
                                         "8-bit digits, 2 passes"),
+    "f32_pairs_2p28_desc": dict(kind="pairs", typed="f32", descending=True, n=1 << 28, end_bit=32, b=8,
+                                desc="2^28 fp32 N(0,1) keys + u32 value pairs (value = original index), "
+                                     "descending, 8-bit digits, 4 passes"),
+    "i32_keys_2p28_asc": dict(kind="keys", typed="i32", descending=False, n=1 << 28, end_bit=32, b=8,
+                              desc="2^28 uniform int32 keys, keys only, ascending, 8-bit digits, 4 passes"),
 }
 
 
@@ -149,7 +154,18 @@ def main():
     dev = torch.device("cuda:0")
 
     log(f"generating {name}")
-    if w["kind"] == "keys":
+    if w["kind"] == "keys" and "typed" in w:
+        keys = workloads.keys_i32_uniform(w["n"])
+        k_in = torch.from_numpy(keys.view(np.int32)).to(dev)
+        del keys
+        n_keys = w["n"]
+        k_out = torch.empty_like(k_in)
+        ws = torch.empty(lrs.radix_sort_workspace_size(n_keys, 0, 32, w["b"], False), dtype=torch.uint8, device=dev)
+
+        def step():
+            lrs.radix_sort_keys_typed(k_in, w["descending"], w["typed"], 0, 32, w["b"], out=k_out, workspace=ws)
+        copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
+    elif w["kind"] == "keys":
         keys = workloads.keys_c1(w["n"]) if w["n"] == 1024 else workloads.keys_c2(w["n"])
         k_in = torch.from_numpy(keys.view(np.int32)).to(dev)
         n_keys = w["n"]
@@ -161,6 +177,20 @@ def main():
             lrs.radix_sort_keys(k_in, 0, w["end_bit"], w["b"], out=k_out, workspace=ws)
         scratch = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
         copy_pair = (scratch[: 1 << 27], scratch[1 << 27:])
+    elif w["kind"] == "pairs" and "typed" in w:
+        keys = workloads.keys_f32_normal(w["n"])
+        k_in = torch.from_numpy(keys.view(np.int32)).to(dev).view(torch.float32)
+        del keys
+        v_in = torch.arange(w["n"], dtype=torch.int32, device=dev)
+        n_keys = w["n"]
+        k_out = torch.empty_like(k_in)
+        v_out = torch.empty_like(v_in)
+        ws = torch.empty(lrs.radix_sort_workspace_size(n_keys, 0, 32, w["b"], True), dtype=torch.uint8, device=dev)
+
+        def step():
+            lrs.radix_sort_pairs_typed(k_in, v_in, w["descending"], w["typed"], 0, 32, w["b"], keys_out=k_out,
+                                       values_out=v_out, workspace=ws)
+        copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
     elif w["kind"] == "pairs":
         keys, vals = workloads.pairs_c3(w["n"], w["dist"])
         k_in = torch.from_numpy(keys.view(np.int32)).to(dev)

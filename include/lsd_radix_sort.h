@@ -50,13 +50,18 @@ typedef enum lrs_status {
     LRS_ERR_SIZE = 4,                /* element count or shape beyond the supported limit */
     LRS_ERR_ALIASING = 5,            /* an output overlaps an input, another output or the workspace */
     LRS_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the *_workspace_size() figure */
-    LRS_ERR_DTYPE = 7,               /* dtype not LRS_DTYPE_FP16 / LRS_DTYPE_BF16 */
+    LRS_ERR_DTYPE = 7,               /* dtype or key_type not one of the values below */
     LRS_ERR_HIP = 8,                 /* the HIP runtime rejected a launch or query */
     LRS_ERR_ALIGNMENT = 9            /* a pointer is not aligned as required (see below) */
 } lrs_status;
 
 #define LRS_DTYPE_FP16 0
 #define LRS_DTYPE_BF16 1
+
+/* 32-bit key types of radix_sort_keys_typed / radix_sort_pairs_typed. */
+#define LRS_KEY_U32 0
+#define LRS_KEY_I32 1
+#define LRS_KEY_F32 2
 
 /* Largest u32 sort: n < 2^32 elements.  Largest segmented row: n < 2^30
  * (FlagTree PR #1084 caps one row at 2^30 elements). */
@@ -94,6 +99,33 @@ int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int
 int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
                      uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stable LSD sort of n 32-bit keys of type key_type, ascending or descending,
+ * with or without a u32 payload.  The sort orders the key's order-preserving
+ * u32 image (100 Days of GPU, Day 35, "Pitfalls": a bijection on the way in,
+ * so floats and signed integers sort as unsigned integers):
+ *   LRS_KEY_U32  the value itself;
+ *   LRS_KEY_I32  two's complement with the sign bit flipped;
+ *   LRS_KEY_F32  IEEE-754 binary32 bits: negative patterns complemented,
+ *                non-negative ones with the sign bit set.  So -0 sorts
+ *                immediately before +0, and NaNs sort by bit pattern beyond
+ *                the infinities (sign-bit-set NaNs first, the others last);
+ * descending (nonzero) sorts the complement of that image, so equal keys keep
+ * their input order in both directions.  [begin_bit, end_bit) selects bits of
+ * the image (0, 32 for a full sort).  The stored key bits are what is moved;
+ * the outputs hold input values, never transformed ones.  Pointers, sizes,
+ * workspace (radix_sort_workspace_size with the same arguments), alignment and
+ * errors are as for radix_sort_keys / radix_sort_pairs; an unknown key_type
+ * returns LRS_ERR_DTYPE.  LRS_KEY_U32 ascending is exactly radix_sort_keys /
+ * radix_sort_pairs.
+ */
+int radix_sort_keys_typed(const void *keys_in, void *keys_out, uint64_t n, int key_type, int descending,
+                          int begin_bit, int end_bit, int digit_bits, void *workspace,
+                          size_t workspace_bytes, void *stream);
+int radix_sort_pairs_typed(const void *keys_in, const uint32_t *vals_in, void *keys_out, uint32_t *vals_out,
+                           uint64_t n, int key_type, int descending, int begin_bit, int end_bit,
+                           int digit_bits, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace segmented_row_sort needs; 0 for rejected arguments or empty input. */
 size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits);

@@ -28,6 +28,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lsd_radix_sort.h")
 LRS_OK = 0
 LRS_DTYPE_FP16 = 0
 LRS_DTYPE_BF16 = 1
+LRS_KEY_U32 = 0
+LRS_KEY_I32 = 1
+LRS_KEY_F32 = 2
 STATUS_NAMES = {
     0: "LRS_OK", 1: "LRS_ERR_NULL_POINTER", 2: "LRS_ERR_BIT_RANGE", 3: "LRS_ERR_DIGIT_BITS",
     4: "LRS_ERR_SIZE", 5: "LRS_ERR_ALIASING", 6: "LRS_ERR_WORKSPACE_TOO_SMALL", 7: "LRS_ERR_DTYPE",
@@ -71,6 +74,10 @@ def load_library():
     lib.radix_sort_digit_histograms.restype = c_int
     lib.radix_sort_copy_probe.argtypes = [P, P, szt, P]
     lib.radix_sort_copy_probe.restype = c_int
+    lib.radix_sort_keys_typed.argtypes = [P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
+    lib.radix_sort_keys_typed.restype = c_int
+    lib.radix_sort_pairs_typed.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
+    lib.radix_sort_pairs_typed.restype = c_int
     lib.radix_sort_set_spin_limit.argtypes = [ctypes.c_uint32]
     lib.radix_sort_set_spin_limit.restype = ctypes.c_uint32
     lib.radix_sort_timing_begin.argtypes = []
@@ -159,6 +166,63 @@ def radix_sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 
     _check(lib.radix_sort_pairs(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, begin_bit,
                                 end_bit, digit_bits, _ptr(workspace), workspace.numel(), _stream(keys)),
            "radix_sort_pairs")
+    return keys_out, values_out
+
+
+_KEY_TYPES = {"u32": LRS_KEY_U32, "i32": LRS_KEY_I32, "f32": LRS_KEY_F32}
+_KEY_DTYPES = {torch.uint32: "u32", torch.int32: "i32", torch.float32: "f32"}
+
+
+def _typed_keys(keys: torch.Tensor, key_type: str | None):
+    if not isinstance(keys, torch.Tensor) or not keys.is_cuda:
+        raise ValueError("keys must be a GPU tensor")
+    if keys.dtype not in _KEY_DTYPES:
+        raise ValueError(f"keys must be uint32, int32 or float32, got {keys.dtype}")
+    if keys.dim() != 1 or not keys.is_contiguous():
+        raise ValueError("keys must be a contiguous 1-D tensor")
+    kt = _KEY_DTYPES[keys.dtype] if key_type is None else key_type
+    if kt not in _KEY_TYPES:
+        raise ValueError(f"key_type must be one of {sorted(_KEY_TYPES)}")
+    return _KEY_TYPES[kt]
+
+
+def radix_sort_keys_typed(keys: torch.Tensor, descending: bool = False, key_type: str | None = None,
+                          begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8,
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Stable sort of 32-bit keys as u32, i32 or f32 (from the dtype unless key_type is given)."""
+    lib = load_library()
+    kt = _typed_keys(keys, key_type)
+    n = keys.numel()
+    if out is None:
+        out = torch.empty_like(keys)
+    if workspace is None:
+        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 0), keys.device)
+    _check(lib.radix_sort_keys_typed(_ptr(keys), _ptr(out), n, kt, int(descending), begin_bit, end_bit,
+                                     digit_bits, _ptr(workspace), workspace.numel(), _stream(keys)),
+           "radix_sort_keys_typed")
+    return out
+
+
+def radix_sort_pairs_typed(keys: torch.Tensor, values: torch.Tensor, descending: bool = False,
+                           key_type: str | None = None, begin_bit: int = 0, end_bit: int = 32,
+                           digit_bits: int = 8, keys_out: torch.Tensor | None = None,
+                           values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """As radix_sort_keys_typed, carrying one 32-bit payload per key; returns (keys, values)."""
+    lib = load_library()
+    kt = _typed_keys(keys, key_type)
+    values = _u32_tensor(values, "values")
+    n = keys.numel()
+    if values.numel() != n:
+        raise ValueError("keys and values differ in length")
+    if keys_out is None:
+        keys_out = torch.empty_like(keys)
+    if values_out is None:
+        values_out = torch.empty_like(values)
+    if workspace is None:
+        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 1), keys.device)
+    _check(lib.radix_sort_pairs_typed(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, kt,
+                                      int(descending), begin_bit, end_bit, digit_bits, _ptr(workspace),
+                                      workspace.numel(), _stream(keys)), "radix_sort_pairs_typed")
     return keys_out, values_out
 
 

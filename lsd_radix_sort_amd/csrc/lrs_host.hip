@@ -250,9 +250,9 @@ void launch_sweep_cfg(const SweepArgs &a, uint64_t tiles, hipStream_t s) {
 
 template <int B, int KK, int PK>
 hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t tiles, hipStream_t s) {
-    // 64-bit look-back words only occur for rows of 2^29 or more elements,
-    // which always take the largest tile.
-    if (wide && KK == kKeyU32)
+    // 64-bit look-back words (and 64-bit store addressing) only occur for rows
+    // of 2^29 or more elements, which always take the largest tile.
+    if (wide)
         launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint64_t>(a, tiles, s);
     else if (cfg == 2)
         launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint32_t>(a, tiles, s);
@@ -317,7 +317,7 @@ hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, hipStream_t 
     return e;
 }
 
-hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint32_t flip,
+hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint32_t flip, uint32_t flip_neg,
                             bool accumulate, hipStream_t s) {
     HistArgs h{};
     h.keys = keys;
@@ -328,11 +328,13 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     h.begin_bit = static_cast<uint32_t>(p.begin_bit);
     h.end_bit = static_cast<uint32_t>(p.end_bit);
     h.flip = flip;
+    h.flip_neg = flip_neg;
     h.atomic = accumulate ? 1u : 0u;
     const uint64_t blocks = p.rows * p.hist_chunks_per_row;
     TimedLaunch t(1, s);
-    hipError_t e = (kk == kKeyU32) ? launch_hist<kKeyU32>(p.b, h, static_cast<uint32_t>(blocks), s)
-                                   : launch_hist<kKeyF16>(p.b, h, static_cast<uint32_t>(blocks), s);
+    hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, static_cast<uint32_t>(blocks), s)
+                   : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, static_cast<uint32_t>(blocks), s)
+                                     : launch_hist<kKeyF16>(p.b, h, static_cast<uint32_t>(blocks), s);
     t.done();
     return e;
 }
@@ -353,6 +355,7 @@ SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass) {
     a.shift = static_cast<uint32_t>(shift);
     a.digit_mask = (1u << width) - 1u;
     a.flip = 0;
+    a.flip_neg = 0;
     a.spin_limit = g_spin_limit;
     return a;
 }
@@ -364,9 +367,24 @@ T *pass_dst(int pass, int passes, T *out, T *alt) {
     return ((passes - 1 - pass) % 2 == 0) ? out : alt;
 }
 
-int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
-             uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int b, void *workspace,
-             size_t ws_bytes, void *stream) {
+// Kernel key kind and transform masks of a (key type, direction); false for an
+// unknown key type.  The masks give each type's order-preserving u32 image and
+// complement it for descending order (see KeyTraits<kKeyX32>).
+bool key_transform(int key_type, int descending, int &kk, uint32_t &flip, uint32_t &flip_neg) {
+    const uint32_t c = descending ? 0xFFFFFFFFu : 0u;
+    switch (key_type) {
+        case LRS_KEY_U32: kk = descending ? kKeyX32 : kKeyU32; flip = c; flip_neg = c; return true;
+        case LRS_KEY_I32: kk = kKeyX32; flip = 0x80000000u ^ c; flip_neg = 0x80000000u ^ c; return true;
+        case LRS_KEY_F32: kk = kKeyX32; flip = 0x80000000u ^ c; flip_neg = 0xFFFFFFFFu ^ c; return true;
+        default: return false;
+    }
+}
+
+// Keys of 32 bits: u32 as they are (KK = kKeyU32), anything else through the
+// two-mask transform (KK = kKeyX32).
+int sort_32(int kk, uint32_t flip, uint32_t flip_neg, bool pairs, const uint32_t *keys_in,
+            const uint32_t *vals_in, uint32_t *keys_out, uint32_t *vals_out, uint64_t n, int begin_bit,
+            int end_bit, int b, void *workspace, size_t ws_bytes, void *stream) {
     if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
@@ -395,14 +413,20 @@ int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint3
         r.row_len = static_cast<uint32_t>(n);
         r.begin_bit = static_cast<uint32_t>(begin_bit);
         r.end_bit = static_cast<uint32_t>(end_bit);
-        const hipError_t e = pairs ? launch_resident<kKeyU32, kResU32>(b, r, 1, n, s)
-                                   : launch_resident<kKeyU32, kResNone>(b, r, 1, n, s);
+        r.flip = flip;
+        r.flip_neg = flip_neg;
+        hipError_t e;
+        if (kk == kKeyU32)
+            e = pairs ? launch_resident<kKeyU32, kResU32>(b, r, 1, n, s) : launch_resident<kKeyU32, kResNone>(b, r, 1, n, s);
+        else
+            e = pairs ? launch_resident<kKeyX32, kResU32>(b, r, 1, n, s) : launch_resident<kKeyX32, kResNone>(b, r, 1, n, s);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kKeyU32, 0, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, s) != hipSuccess)
+        return LRS_ERR_HIP;
 
     uint32_t *alt_k = reinterpret_cast<uint32_t *>(ws + p.off_alt_keys);
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
@@ -413,16 +437,20 @@ int sort_u32(bool pairs, const uint32_t *keys_in, const uint32_t *vals_in, uint3
         uint32_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
         a.keys_in = src_k;
         a.keys_out = dk;
+        a.flip = flip;
+        a.flip_neg = flip_neg;
         hipError_t e;
         TimedLaunch t(2, s);
         if (pairs) {
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = launch_sweep<kKeyU32, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX32, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
             src_v = dv;
         } else {
-            e = launch_sweep<kKeyU32, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX32, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -449,15 +477,37 @@ size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int dig
 int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int begin_bit,
                     int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
                     void *stream) {
-    return sort_u32(false, keys_in, nullptr, keys_out, nullptr, n, begin_bit, end_bit, digit_bits,
-                    workspace, workspace_bytes, stream);
+    return sort_32(kKeyU32, 0, 0, false, keys_in, nullptr, keys_out, nullptr, n, begin_bit, end_bit,
+                   digit_bits, workspace, workspace_bytes, stream);
 }
 
 int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
                      uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
                      void *workspace, size_t workspace_bytes, void *stream) {
-    return sort_u32(true, keys_in, vals_in, keys_out, vals_out, n, begin_bit, end_bit, digit_bits,
-                    workspace, workspace_bytes, stream);
+    return sort_32(kKeyU32, 0, 0, true, keys_in, vals_in, keys_out, vals_out, n, begin_bit, end_bit,
+                   digit_bits, workspace, workspace_bytes, stream);
+}
+
+int radix_sort_keys_typed(const void *keys_in, void *keys_out, uint64_t n, int key_type, int descending,
+                          int begin_bit, int end_bit, int digit_bits, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    int kk;
+    uint32_t flip, flip_neg;
+    if (!key_transform(key_type, descending, kk, flip, flip_neg)) return LRS_ERR_DTYPE;
+    return sort_32(kk, flip, flip_neg, false, static_cast<const uint32_t *>(keys_in), nullptr,
+                   static_cast<uint32_t *>(keys_out), nullptr, n, begin_bit, end_bit, digit_bits, workspace,
+                   workspace_bytes, stream);
+}
+
+int radix_sort_pairs_typed(const void *keys_in, const uint32_t *vals_in, void *keys_out, uint32_t *vals_out,
+                           uint64_t n, int key_type, int descending, int begin_bit, int end_bit,
+                           int digit_bits, void *workspace, size_t workspace_bytes, void *stream) {
+    int kk;
+    uint32_t flip, flip_neg;
+    if (!key_transform(key_type, descending, kk, flip, flip_neg)) return LRS_ERR_DTYPE;
+    return sort_32(kk, flip, flip_neg, true, static_cast<const uint32_t *>(keys_in), vals_in,
+                   static_cast<uint32_t *>(keys_out), vals_out, n, begin_bit, end_bit, digit_bits, workspace,
+                   workspace_bytes, stream);
 }
 
 size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits) {
@@ -508,7 +558,7 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
 
     uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
     uint32_t *idx[2] = {reinterpret_cast<uint32_t *>(ws + p.off_idx[0]),
@@ -525,15 +575,15 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
         if (pass == 0) {
             a.vals_in = nullptr;
             a.vals_out = idx[0];
-            e = launch_sweep<kKeyF16, kPayIdxFirst>(digit_bits, a, p.tile_cfg, false, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayIdxFirst>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         } else if (pass + 1 < p.passes) {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx[pass & 1];
-            e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, p.tile_cfg, false, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         } else {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx_out;
-            e = launch_sweep<kKeyF16, kPayIdxLast>(digit_bits, a, p.tile_cfg, false, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayIdxLast>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -562,7 +612,7 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
         if (e != hipSuccess) return LRS_ERR_HIP;
     }
     if (n == 0) return LRS_OK;
-    return launch_histogram(p, keys, hist_out, kKeyU32, 0, true, s) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    return launch_histogram(p, keys, hist_out, kKeyU32, 0, 0, true, s) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
 int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream) {

@@ -49,7 +49,7 @@ constexpr uint32_t kXcdChunk = LRS_XCD_CHUNK;
 constexpr uint32_t kXcds = 8;          // accelerator complex dies (XCDs) of an MI355X
 constexpr int kWave = 64;              // CDNA wavefront width
 
-enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1 };
+enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1, kKeyX32 = 2 };
 
 // Payload handling of one pass.
 enum PayKind : int {
@@ -63,10 +63,13 @@ enum PayKind : int {
 
 template <int KK> struct KeyTraits;
 
+// key(v, flip, flip_neg) maps a stored pattern to the unsigned integer whose
+// ascending order is the wanted order.
+
 template <> struct KeyTraits<kKeyU32> {
     using Stored = uint32_t;
     // The sort key of a stored u32 is the value itself.
-    __device__ static inline uint32_t key(uint32_t v, uint32_t) { return v; }
+    __device__ static inline uint32_t key(uint32_t v, uint32_t, uint32_t) { return v; }
 };
 
 template <> struct KeyTraits<kKeyF16> {
@@ -74,9 +77,20 @@ template <> struct KeyTraits<kKeyF16> {
     // Order-preserving key of a 16-bit float pattern: complement negatives,
     // set the sign bit of non-negatives; `flip` = 0xFFFF complements the result
     // for descending order.
-    __device__ static inline uint32_t key(uint32_t v, uint32_t flip) {
+    __device__ static inline uint32_t key(uint32_t v, uint32_t flip, uint32_t) {
         uint32_t asc = v ^ ((v & 0x8000u) ? 0xFFFFu : 0x8000u);
         return asc ^ flip;
+    }
+};
+
+template <> struct KeyTraits<kKeyX32> {
+    using Stored = uint32_t;
+    // Any other 32-bit key: XOR with `flip` when the sign bit is clear and with
+    // `flip_neg` when it is set.  Signed integers: both 0x80000000.  Floats:
+    // 0x80000000 and 0xFFFFFFFF (set the sign bit of non-negatives, complement
+    // negatives).  Descending order complements both masks (u32: both ~0).
+    __device__ static inline uint32_t key(uint32_t v, uint32_t flip, uint32_t flip_neg) {
+        return v ^ ((static_cast<int32_t>(v) < 0) ? flip_neg : flip);
     }
 };
 
@@ -217,7 +231,8 @@ struct SweepArgs {
     uint32_t hist_row_stride;
     uint32_t shift;          // lowest bit of this pass's digit
     uint32_t digit_mask;     // (1 << width) - 1
-    uint32_t flip;           // 0xFFFF for descending 16-bit float keys, else 0
+    uint32_t flip;           // key transform masks (see KeyTraits)
+    uint32_t flip_neg;
     uint32_t spin_limit;     // polls of an unpublished look-back word before the tile counts
                              // its prefix from the keys; 0: always count from the keys
 };
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t p = wbase + j * kWave + lane;
-            const uint32_t dig = (KeyTraits<KK>::key(key[j], a.flip) >> a.shift) & a.digit_mask;
+            const uint32_t dig = (KeyTraits<KK>::key(key[j], a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
             const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
             uint32_t below, size;
             if constexpr (MATCH == kMatchBallot) {
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
             __syncthreads();
             const Stored *row_keys = static_cast<const Stored *>(a.keys_in) + row_base;
             for (uint32_t i = tid; i < tile_start; i += BLOCK) {
-                const uint32_t d = (KeyTraits<KK>::key(row_keys[i], a.flip) >> a.shift) & a.digit_mask;
+                const uint32_t d = (KeyTraits<KK>::key(row_keys[i], a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
                 atomicAdd(&s_goff[d], 1u);
             }
             __syncthreads();
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     for (int i = 0; i < ITEMS; ++i) {
         const uint32_t k = i * BLOCK + tid;
         const uint32_t v = s_buf[k];
-        const uint32_t d = (KeyTraits<KK>::key(v, a.flip) >> a.shift) & a.digit_mask;
+        const uint32_t d = (KeyTraits<KK>::key(v, a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
         if constexpr (PK != kPayNone) s_dig[k] = static_cast<uint8_t>(d);
         const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
         if constexpr (kWide) {
@@ -546,7 +561,8 @@ struct ResidentArgs {
     uint32_t row_len;        // elements per row, at most BLOCK * ITEMS
     uint32_t begin_bit;
     uint32_t end_bit;
-    uint32_t flip;           // 0xFFFF for descending 16-bit float keys, else 0
+    uint32_t flip;           // key transform masks (see KeyTraits)
+    uint32_t flip_neg;
 };
 
 // Payload of the resident sort.
@@ -616,7 +632,7 @@ __global__ __launch_bounds__(BLOCK) void resident_sort_kernel(ResidentArgs a) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t p = wbase + j * kWave + lane;
-            const uint32_t d = (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip) >> shift) & mask) : (R - 1u);
+            const uint32_t d = (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip, a.flip_neg) >> shift) & mask) : (R - 1u);
             uint32_t below, size;
             group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
             const uint32_t before = s_cnt[wave][d];
@@ -688,7 +704,8 @@ struct HistArgs {
     uint32_t passes;
     uint32_t begin_bit;
     uint32_t end_bit;
-    uint32_t flip;
+    uint32_t flip;           // key transform masks (see KeyTraits)
+    uint32_t flip_neg;
     uint32_t atomic;         // 1: several workgroups per row accumulate; 0: one writes it
 };
 
@@ -724,7 +741,7 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
 
     uint32_t *mine = s_h + (threadIdx.x % kHistCopies);
     auto count_key = [&](uint32_t v) {
-        const uint32_t k = KeyTraits<KK>::key(v, a.flip);
+        const uint32_t k = KeyTraits<KK>::key(v, a.flip, a.flip_neg);
 #pragma unroll
         for (int p = 0; p < kMaxPasses; ++p) {
             if (p < static_cast<int>(a.passes)) {
@@ -736,7 +753,7 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
         }
     };
     auto count_vec = [&](const uint4 &w) {
-        if constexpr (KK == kKeyU32) {
+        if constexpr (sizeof(Stored) == 4) {
             count_key(w.x); count_key(w.y); count_key(w.z); count_key(w.w);
         } else {
             count_key(w.x & 0xFFFFu); count_key(w.x >> 16);

@@ -73,6 +73,10 @@ def _load():
     lib.oracle_segmented_histograms.restype = c_int
     lib.oracle_row_stable_position.argtypes = [P, u64, c_int, u64]
     lib.oracle_row_stable_position.restype = u64
+    lib.oracle_key32.argtypes = [u32, c_int, c_int, P]
+    lib.oracle_key32.restype = c_int
+    lib.oracle_radix_sort_typed.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int]
+    lib.oracle_radix_sort_typed.restype = c_int
     _lib = lib
     return lib
 
@@ -166,6 +170,34 @@ def radix_sort_keys(keys, begin_bit: int = 0, end_bit: int = 32, digit_bits: int
 def stable_position(keys: np.ndarray, begin_bit: int, end_bit: int, i: int) -> int:
     k = _u32(keys)
     return int(_load().oracle_stable_position(_ptr(k), k.size, begin_bit, end_bit, int(i)))
+
+
+# ------------------------------------------------------ typed 32-bit keys
+
+KEY_TYPES = {"u32": 0, "i32": 1, "f32": 2}
+
+
+def key32(bits: int, key_type: str, descending: bool = False) -> int:
+    """Order-preserving u32 image of one 32-bit pattern of the given type."""
+    out = np.zeros(1, dtype=np.uint32)
+    _check(_load().oracle_key32(int(bits) & 0xFFFFFFFF, KEY_TYPES[key_type], int(descending), _ptr(out)),
+           "key32")
+    return int(out[0])
+
+
+def radix_sort_typed(keys, vals=None, key_type: str = "u32", descending: bool = False,
+                     begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8):
+    """Stable sort of 32-bit keys (bit patterns of u32, i32 or f32) by their image's
+    bit window; returns (key patterns, vals-or-None) in sorted order."""
+    k = np.ascontiguousarray(np.asarray(keys).view(np.uint32))
+    v = None if vals is None else _u32(vals)
+    if v is not None and v.size != k.size:
+        raise ValueError("keys and vals differ in length")
+    ko = np.empty_like(k)
+    vo = None if v is None else np.empty_like(v)
+    _check(_load().oracle_radix_sort_typed(_ptr(k), _ptr(v), _ptr(ko), _ptr(vo), k.size, KEY_TYPES[key_type],
+                                           int(descending), begin_bit, end_bit, digit_bits), "radix_sort_typed")
+    return ko, vo
 
 
 # ------------------------------------------------------- 16-bit float rows

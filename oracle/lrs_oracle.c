@@ -27,6 +27,8 @@
  *    the descending flag into that conversion).  Reading: negative patterns are
  *    bit-complemented, non-negative patterns get the sign bit set; descending
  *    is the complement of the ascending key, so ties keep input order.
+ *  - The same kind of map for 32-bit signed integers and binary32 floats, and
+ *    the stable sort of such keys (with an optional payload) by their image.
  *
  * Every result here is unique (a stable sort of a fixed sequence has exactly one
  * output), so the GPU path is compared against it element for element.
@@ -243,6 +245,71 @@ uint64_t oracle_stable_position(const uint32_t *keys, uint64_t n, int begin_bit,
         if (kj < ki || (kj == ki && j < i)) pos++;
     }
     return pos;
+}
+
+/* ------------------------------------------------------ typed 32-bit keys */
+
+/*
+ * Order-preserving u32 image of a 32-bit key (100 Days of GPU, Day 35,
+ * "Pitfalls": floats and signed integers sort as unsigned integers after a
+ * bijection on the way in).  key_type 0 = u32: the value.  1 = i32: adding 2^31
+ * modulo 2^32 carries INT32_MIN..INT32_MAX onto 0..UINT32_MAX in order.
+ * 2 = f32 (IEEE binary32, sign-magnitude): a negative pattern is complemented,
+ * so larger magnitudes come first, and a non-negative one gets its sign bit
+ * set, so it lands above every negative.  Descending: the complement of the
+ * ascending image, so equal keys keep their input order.  Readings: -0 sorts
+ * just before +0; NaN patterns sort by their image, beyond the infinities.
+ */
+int oracle_key32(uint32_t bits, int key_type, int descending, uint32_t *out)
+{
+    uint32_t asc;
+    if (key_type == 0) {
+        asc = bits;
+    } else if (key_type == 1) {
+        asc = bits + 0x80000000u;
+    } else if (key_type == 2) {
+        asc = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    } else {
+        return ORACLE_EINVAL;
+    }
+    *out = descending ? ~asc : asc;
+    return ORACLE_OK;
+}
+
+/*
+ * Stable sort of n typed 32-bit keys (and an optional u32 payload) by the bit
+ * window [begin_bit, end_bit) of their image: the (image, input index) pairs go
+ * through the LSD oracle above, then the original key bits and payloads are
+ * gathered in the sorted index order.
+ */
+int oracle_radix_sort_typed(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+                            uint32_t *vals_out, uint64_t n, int key_type, int descending,
+                            int begin_bit, int end_bit, int digit_bits)
+{
+    if (!check_window(begin_bit, end_bit, 32, digit_bits) || n > 0xFFFFFFFFull) return ORACLE_EINVAL;
+    if (n == 0) return ORACLE_OK;
+    if (!keys_in || !keys_out || ((vals_in == NULL) != (vals_out == NULL))) return ORACLE_EINVAL;
+    uint32_t *image = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    uint32_t *index = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    uint32_t *image_sorted = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    uint32_t *index_sorted = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    int rc = ORACLE_OK;
+    if (!image || !index || !image_sorted || !index_sorted) { rc = ORACLE_ENOMEM; goto done; }
+    for (uint64_t i = 0; i < n; i++) {
+        rc = oracle_key32(keys_in[i], key_type, descending, &image[i]);
+        if (rc != ORACLE_OK) goto done;
+        index[i] = (uint32_t)i;
+    }
+    rc = oracle_radix_sort_pairs(image, index, image_sorted, index_sorted, n, begin_bit, end_bit,
+                                 digit_bits, 0);
+    if (rc != ORACLE_OK) goto done;
+    for (uint64_t i = 0; i < n; i++) {
+        keys_out[i] = keys_in[index_sorted[i]];
+        if (vals_in) vals_out[i] = vals_in[index_sorted[i]];
+    }
+done:
+    free(image); free(index); free(image_sorted); free(index_sorted);
+    return rc;
 }
 
 /* ------------------------------------------------- fp16 / bf16 row sorting */

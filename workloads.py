@@ -111,6 +111,11 @@ WORKLOADS = {
                                    dtype="fp16", descending=False, digit_bits=(4,)),
     "c5_bf16_4096x4096_desc": dict(index=4, kind="segmented", rows=4096, cols=4096,
                                    dtype="bf16", descending=True, digit_bits=(8,)),
+    # typed 32-bit keys (not one of the five configurations; the same sizes as the pair sort)
+    "f32_pairs_2p28_desc": dict(index=5, kind="typed_pairs", n=1 << 28, key_type="f32",
+                                descending=True, digit_bits=(8,)),
+    "i32_keys_2p28_asc": dict(index=6, kind="typed_keys", n=1 << 28, key_type="i32",
+                              descending=False, digit_bits=(8,)),
 }
 
 
@@ -147,6 +152,17 @@ def matrix_c4(rows: int = 1024, cols: int = 65536) -> np.ndarray:
 
 def matrix_c5(rows: int = 4096, cols: int = 4096) -> np.ndarray:
     return bf16_64level_bits(seed_of(4), rows * cols).reshape(rows, cols)
+
+
+def keys_f32_normal(n: int = 1 << 28) -> np.ndarray:
+    """Bit patterns (uint32) of N(0,1) draws (Box-Muller in fp64) rounded to
+    binary32; the typed-key workload."""
+    return normal_f64(seed_of(5), n).astype(np.float32).view(np.uint32)
+
+
+def keys_i32_uniform(n: int = 1 << 28) -> np.ndarray:
+    """Bit patterns (uint32) of uniform signed 32-bit integers."""
+    return uniform_u32(seed_of(6), n)
 
 
 def random_u32(seed: int, n: int) -> np.ndarray:
