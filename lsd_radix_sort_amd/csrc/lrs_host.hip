@@ -42,8 +42,8 @@ constexpr uint64_t kMinTiles = LRS_MIN_TILES;
 constexpr uint64_t kResidentMax = 8192;
 
 // The largest tile shape with at least kMinTiles tiles and at most 1/32 of
-// its elements past row ends (rows of 65536 take 8192-key tiles, not five
-// 14336-key tiles with 8.6% padding).
+// its elements past row ends (rows of 65536 take eight 8192-key tiles, not
+// five 15360-key tiles with 15% padding).
 int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
     for (int c = 2; c >= 1; --c) {
         const uint64_t tile = kTileCfgs[c].tile;

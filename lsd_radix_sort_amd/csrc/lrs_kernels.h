@@ -27,7 +27,7 @@ namespace lrs {
 
 // Compile-time tunables (defaults are the measured choices).
 #ifndef LRS_SWEEP_ITEMS
-#define LRS_SWEEP_ITEMS 28      // keys per thread in the largest sweep tile
+#define LRS_SWEEP_ITEMS 30      // keys per thread in the largest sweep tile
 #endif
 #ifndef LRS_SWEEP_BLOCK
 #define LRS_SWEEP_BLOCK 512     // threads per workgroup of the largest sweep tile
@@ -307,10 +307,11 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
 
     // s_buf holds the tile in digit order (keys, then payload); during the
     // ranking its front holds the per-wave digit masks of the LDS matching.
+    // Between writing the keys and the payload out of the same slots, each
+    // thread keeps its slots' digits in registers, four to a word.
     __shared__ uint32_t s_buf[TILE];
     __shared__ uint32_t s_cnt[WAVES][R];      // per-wave digit counts, then per-wave bases
     __shared__ uint32_t s_goff[R];            // output index of digit run start minus local start
-    __shared__ uint8_t s_dig[PK != kPayNone ? TILE : 1];  // digit of each slot, for the payload
     __shared__ uint32_t s_tmp[WAVES];
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_gave_up;            // a look-back wave stopped waiting
@@ -510,13 +511,16 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     // every real element; the range check of the buffer store only keeps a
     // logic error from becoming a stray store.
     Stored *kout = static_cast<Stored *>(a.keys_out) + row_base;
+    uint32_t slot_digits[(ITEMS + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (ITEMS + 3) / 4; ++i) slot_digits[i] = 0u;
     const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const uint32_t k = i * BLOCK + tid;
         const uint32_t v = s_buf[k];
         const uint32_t d = (KeyTraits<KK>::key(v, a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
-        if constexpr (PK != kPayNone) s_dig[k] = static_cast<uint8_t>(d);
+        if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
         const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
         if constexpr (kWide) {
             if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
@@ -541,7 +545,8 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
             const uint32_t k = i * BLOCK + tid;
-            const uint32_t dst = (k < valid) ? s_goff[s_dig[k]] + k : 0xFFFFFFFFu;
+            const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
+            const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
             if constexpr (kWide) {
                 if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_buf[k]);
             } else {

@@ -99,7 +99,7 @@ def test_c3_pairs_reduced_size(dist):
 
 @pytest.mark.parametrize("b,dist", [(8, "uniform"), (4, "and3")])
 def test_large_tile_configuration(b, dist):
-    # enough elements for the largest sweep tile (at least 1024 tiles of 14336)
+    # enough elements for the largest sweep tile (at least 256 tiles of 15360)
     n = 15_000_007
     keys = workloads.random_u32(4000 + b, n)
     if dist == "and3":
@@ -115,7 +115,7 @@ def test_large_tile_configuration(b, dist):
 
 @pytest.mark.parametrize("b,dist", [(8, "and3"), (4, "uniform")])
 def test_mid_tile_configuration(b, dist):
-    # too few elements for 256 tiles of 14336, enough for 256 of 8192
+    # too few elements for 256 tiles of 15360, enough for 256 of 8192
     n = 3_000_017
     keys = workloads.random_u32(4300 + b, n)
     if dist == "and3":

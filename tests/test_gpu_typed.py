@@ -1,7 +1,7 @@
 """GPU parity of the typed 32-bit sorts (signed integers, binary32 floats and
 descending u32) against the CPU oracle, element for element with tolerance 0,
 keys-only and with a payload, across the whole-row, 4096-, 8192- and
-14336-key tile shapes, with special float patterns mixed in."""
+15360-key tile shapes, with special float patterns mixed in."""
 import sys
 
 import numpy as np
