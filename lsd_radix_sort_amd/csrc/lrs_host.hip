@@ -55,10 +55,11 @@ int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
 }
 constexpr uint64_t kAlign = 256;
 #ifndef LRS_HIST_BLOCKS
-#define LRS_HIST_BLOCKS 2048
+#define LRS_HIST_BLOCKS 512
 #endif
-// Histogram workgroups per launch (measured on 2^28 keys: 2048 spans beat
-// 640, 1280, 2560 and 5120, and beat interleaved strips).
+// Histogram workgroups per launch: 1024 threads and 128 KB of LDS counters
+// each, so one per CU at a time (measured on 2^28 keys against 256 and, with
+// smaller workgroups and fewer copies, 640 to 5120).
 constexpr uint32_t kHistTargetBlocks = LRS_HIST_BLOCKS;
 #ifndef LRS_HIST_MIN_CHUNK
 #define LRS_HIST_MIN_CHUNK 16384
@@ -209,7 +210,7 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 template <int B, int KK>
 hipError_t launch_hist_b(const HistArgs &a, uint32_t blocks, hipStream_t s) {
-    histogram_kernel<B, KK><<<blocks, kBlock, 0, s>>>(a);
+    histogram_kernel<B, KK><<<blocks, kHistBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ namespace lrs {
 #define LRS_LOOKBACK 4          // predecessor words a look-back lane reads per round trip
 #endif
 #ifndef LRS_HIST_COPIES
-#define LRS_HIST_COPIES 8       // LDS copies of the histogram, lanes spread over them
+#define LRS_HIST_COPIES 32      // LDS copies of the histogram, lane l counts into copy l % 32
 #endif
 #ifndef LRS_XCD_CHUNK
 #define LRS_XCD_CHUNK 16        // consecutive sweep tiles handed to one XCD at a time
@@ -716,19 +716,24 @@ struct HistArgs {
 
 constexpr int kHistMaxCounters = 1024;  // passes * R for every legal (window, b)
 constexpr int kHistCopies = LRS_HIST_COPIES;
+#ifndef LRS_HIST_BLOCK
+#define LRS_HIST_BLOCK 1024
+#endif
+constexpr int kHistBlock = LRS_HIST_BLOCK;  // threads per histogram workgroup
 #ifndef LRS_HIST_INTERLEAVE
 #define LRS_HIST_INTERLEAVE 0   // 0: one span of the row per workgroup; 1: 4 KiB strips in turn
 #endif
 
 // Counts every pass's digit over one share of one row in LDS, from one read of
 // the keys with 16-byte loads, then adds the counts to the row's histogram.
-// Lane l counts into copy l % kHistCopies of the counters (copies of one
-// counter sit in consecutive words), so lanes that share a digit mostly hit
-// different LDS banks instead of serialising on one address.  The pass loop
+// Lane l counts into copy l % kHistCopies of the counters, and the copies of
+// one counter sit in consecutive words: with 32 copies a lane's LDS bank
+// depends on its lane alone, whatever the digits, and lanes that share a
+// digit do not serialise on one address (except lanes l and l + 32).  The pass loop
 // is unrolled: each pass costs one bit-field extract, one address add and one
 // LDS add whose pass offset is an immediate.
 template <int B, int KK>
-__global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
+__global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t R = 1u << B;
     using Stored = typename KeyTraits<KK>::Stored;
     constexpr uint32_t kPerVec = 16u / sizeof(Stored);
@@ -736,12 +741,12 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t kPassWords = R * kHistCopies;
     static_assert(kMaxPasses * R <= kHistMaxCounters, "counters must fit");
     constexpr int kUnroll = 4;
-    __shared__ uint32_t s_h[kHistMaxCounters * kHistCopies];
+    __shared__ uint32_t s_h[kMaxPasses * R * kHistCopies];  // 128 KB for 8-bit digits of u32 keys
 
     const uint32_t row = blockIdx.x / a.chunks_per_row;
     const uint32_t chunk = blockIdx.x - row * a.chunks_per_row;
     const uint32_t total = a.passes * R;
-    for (uint32_t i = threadIdx.x; i < total * kHistCopies; i += kBlock) s_h[i] = 0u;
+    for (uint32_t i = threadIdx.x; i < total * kHistCopies; i += kHistBlock) s_h[i] = 0u;
     __syncthreads();
 
     uint32_t *mine = s_h + (threadIdx.x % kHistCopies);
@@ -778,12 +783,12 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     const uint4 *v4 = reinterpret_cast<const uint4 *>(base + head);
 
 #if LRS_HIST_INTERLEAVE
-    const uint32_t step = a.chunks_per_row * kBlock;
-    uint32_t q = chunk * kBlock + threadIdx.x;
+    const uint32_t step = a.chunks_per_row * kHistBlock;
+    uint32_t q = chunk * kHistBlock + threadIdx.x;
     const uint32_t q_end = nvec;
 #else
     const uint32_t per = (nvec + a.chunks_per_row - 1) / a.chunks_per_row;
-    const uint32_t step = kBlock;
+    const uint32_t step = kHistBlock;
     uint32_t q = chunk * per + threadIdx.x;
     const uint32_t q_end = min(nvec, chunk * per + per);
 #endif
@@ -801,11 +806,13 @@ __global__ __launch_bounds__(kBlock) void histogram_kernel(HistArgs a) {
     __syncthreads();
 
     uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
-    for (uint32_t i = threadIdx.x; i < total; i += kBlock) {
+    for (uint32_t i = threadIdx.x; i < total; i += kHistBlock) {
         const uint32_t p = i / R, d = i - p * R;
         uint32_t c = 0;
+        // copies taken in a rotated order so neighbouring threads read different banks
 #pragma unroll
-        for (int k = 0; k < kHistCopies; ++k) c += s_h[p * kPassWords + d * kHistCopies + k];
+        for (int k = 0; k < kHistCopies; ++k)
+            c += s_h[p * kPassWords + d * kHistCopies + ((k + i) % kHistCopies)];
         if (a.atomic) {
             if (c) atomicAdd(out + i, c);
         } else {
