@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--dist", default=None, choices=["uniform", "and3"],
                     help="shorthand for the 2^28-pair workload with this key distribution")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scan", default="lookback", choices=["lookback", "reduce-then-scan"],
+                    help="offset strategy of single-row sorts (the A/B of the two)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -151,6 +153,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lrs.load_library()
+    lrs.radix_sort_set_scan_strategy(args.scan)
     dev = torch.device("cuda:0")
 
     log(f"generating {name}")
@@ -277,14 +280,14 @@ def main():
         "dtype": "u16" if w["kind"] == "rows" else "u32",
         "data": "synthetic",
         "config": {"workload": w["desc"], "name": name, "n": n_keys, "digit_bits": w["b"],
-                   "passes": launches_per_sort},
+                   "passes": launches_per_sort, "scan": args.scan},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": MEASURED_SWEEP_TRAFFIC.get(name),
+            "traffic": MEASURED_SWEEP_TRAFFIC.get(name) if args.scan == "lookback" else None,
             "kernel": "resident_sort_kernel (whole row, all passes in LDS)" if resident
                       else "sweep_kernel (one LSD pass)",
             "bytes_per_launch": bytes_sort // max(launches_per_sort, 1),

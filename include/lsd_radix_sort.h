@@ -180,10 +180,29 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
 uint32_t radix_sort_set_spin_limit(uint32_t polls);
 
 /*
+ * How single-row sorts (radix_sort_keys/pairs and the typed forms) get each
+ * tile's output offsets (CUDA Handbook ch.16: scan of the per-block counts;
+ * FlagTree PR #1084 step 2 compares look-back with precomputed offsets):
+ *   LRS_SCAN_LOOKBACK (default)  one launch per pass; each tile publishes its
+ *       digit counts and adds up its predecessors' (decoupled look-back).
+ *   LRS_SCAN_REDUCE_THEN_SCAN  three launches per pass: count the digit over
+ *       each of up to 512 partitions of whole tiles, scan those counts into
+ *       start offsets, then sort each partition's tiles in order from them;
+ *       the keys are read once more per pass.
+ * The result is identical.  Segmented row sorts always use the look-back.
+ * Applies to sorts enqueued after the call; returns the previous strategy, or
+ * -1 (and changes nothing) for an unknown one.  Not thread-safe.
+ */
+#define LRS_SCAN_LOOKBACK 0
+#define LRS_SCAN_REDUCE_THEN_SCAN 1
+int radix_sort_set_scan_strategy(int strategy);
+
+/*
  * Kernel timing for measurement.  After radix_sort_timing_begin(), every
  * kernel the library enqueues is bracketed by HIP events on its stream.
  * radix_sort_timing_end() waits for those events and reports, per kernel kind
- * (0 = workspace clear, 1 = digit histogram, 2 = sweep/scatter pass,
+ * (0 = workspace clear, 1 = digit histogram (and the reduce-then-scan count
+ * and scan), 2 = sweep/scatter pass,
  * 3 = copy probe, 4 = whole-row resident sort), the summed milliseconds and
  * the number of launches, then stops recording.  Arrays have 5 entries.  At
  * most 65536 launches are timed.

@@ -31,6 +31,9 @@ LRS_DTYPE_BF16 = 1
 LRS_KEY_U32 = 0
 LRS_KEY_I32 = 1
 LRS_KEY_F32 = 2
+LRS_SCAN_LOOKBACK = 0
+LRS_SCAN_REDUCE_THEN_SCAN = 1
+_SCAN_STRATEGIES = {"lookback": LRS_SCAN_LOOKBACK, "reduce-then-scan": LRS_SCAN_REDUCE_THEN_SCAN}
 STATUS_NAMES = {
     0: "LRS_OK", 1: "LRS_ERR_NULL_POINTER", 2: "LRS_ERR_BIT_RANGE", 3: "LRS_ERR_DIGIT_BITS",
     4: "LRS_ERR_SIZE", 5: "LRS_ERR_ALIASING", 6: "LRS_ERR_WORKSPACE_TOO_SMALL", 7: "LRS_ERR_DTYPE",
@@ -78,6 +81,8 @@ def load_library():
     lib.radix_sort_keys_typed.restype = c_int
     lib.radix_sort_pairs_typed.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
     lib.radix_sort_pairs_typed.restype = c_int
+    lib.radix_sort_set_scan_strategy.argtypes = [c_int]
+    lib.radix_sort_set_scan_strategy.restype = c_int
     lib.radix_sort_set_spin_limit.argtypes = [ctypes.c_uint32]
     lib.radix_sort_set_spin_limit.restype = ctypes.c_uint32
     lib.radix_sort_timing_begin.argtypes = []
@@ -272,6 +277,15 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst smaller than src")
     _check(lib.radix_sort_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src)), "copy_probe")
+
+
+def radix_sort_set_scan_strategy(strategy: str) -> str:
+    """How single-row sorts find each tile's output offsets: "lookback" (default)
+    or "reduce-then-scan".  Returns the previous strategy."""
+    if strategy not in _SCAN_STRATEGIES:
+        raise ValueError(f"strategy must be one of {sorted(_SCAN_STRATEGIES)}")
+    old = load_library().radix_sort_set_scan_strategy(_SCAN_STRATEGIES[strategy])
+    return {v: k for k, v in _SCAN_STRATEGIES.items()}[old]
 
 
 def radix_sort_set_spin_limit(polls: int) -> int:

@@ -116,6 +116,11 @@ struct TimedLaunch {
 constexpr uint32_t kDefaultSpinLimit = 1u << 16;
 uint32_t g_spin_limit = kDefaultSpinLimit;
 
+// Scan strategy of single-row sorts (LRS_SCAN_*); segmented rows always use the look-back.
+int g_scan_strategy = LRS_SCAN_LOOKBACK;
+// Partitions of the reduce-then-scan path: two workgroups per CU.
+constexpr uint64_t kPartitions = 512;
+
 // ------------------------------------------------------------ planning
 
 struct Plan {
@@ -240,38 +245,51 @@ int match_kind() {
     return kind;
 }
 
-template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W>
-void launch_sweep_cfg(const SweepArgs &a, uint64_t tiles, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(tiles));
-    if (match_kind() == kMatchBallot)
-        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchBallot><<<grid, BLOCK, 0, s>>>(a);
+// `grid` workgroups: one per tile (look-back), or one per partition (PART).
+template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, bool PART>
+void launch_sweep_cfg(const SweepArgs &a, uint64_t grid_size, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(grid_size));
+    if (PART || match_kind() == kMatchBallot)
+        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchBallot, PART><<<grid, BLOCK, 0, s>>>(a);
     else
-        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchLds><<<grid, BLOCK, 0, s>>>(a);
+        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchLds, false><<<grid, BLOCK, 0, s>>>(a);
 }
 
-template <int B, int KK, int PK>
-hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t tiles, hipStream_t s) {
+template <int B, int KK, int PK, bool PART>
+hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s) {
     // 64-bit look-back words (and 64-bit store addressing) only occur for rows
     // of 2^29 or more elements, which always take the largest tile.
     if (wide)
-        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint64_t>(a, tiles, s);
+        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint64_t, PART>(a, grid, s);
     else if (cfg == 2)
-        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint32_t>(a, tiles, s);
+        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint32_t, PART>(a, grid, s);
     else if (cfg == 1)
-        launch_sweep_cfg<B, kTileCfgs[1].items, kTileCfgs[1].block, KK, PK, uint32_t>(a, tiles, s);
+        launch_sweep_cfg<B, kTileCfgs[1].items, kTileCfgs[1].block, KK, PK, uint32_t, PART>(a, grid, s);
     else
-        launch_sweep_cfg<B, kTileCfgs[0].items, kTileCfgs[0].block, KK, PK, uint32_t>(a, tiles, s);
+        launch_sweep_cfg<B, kTileCfgs[0].items, kTileCfgs[0].block, KK, PK, uint32_t, PART>(a, grid, s);
     return hipGetLastError();
 }
 
-template <int KK, int PK>
-hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t tiles, hipStream_t s) {
+template <int KK, int PK, bool PART = false>
+hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s) {
     switch (b) {
-        case 1: return launch_sweep_b<1, KK, PK>(a, cfg, wide, tiles, s);
-        case 2: return launch_sweep_b<2, KK, PK>(a, cfg, wide, tiles, s);
-        case 4: return launch_sweep_b<4, KK, PK>(a, cfg, wide, tiles, s);
-        default: return launch_sweep_b<8, KK, PK>(a, cfg, wide, tiles, s);
+        case 1: return launch_sweep_b<1, KK, PK, PART>(a, cfg, wide, grid, s);
+        case 2: return launch_sweep_b<2, KK, PK, PART>(a, cfg, wide, grid, s);
+        case 4: return launch_sweep_b<4, KK, PK, PART>(a, cfg, wide, grid, s);
+        default: return launch_sweep_b<8, KK, PK, PART>(a, cfg, wide, grid, s);
     }
+}
+
+template <int KK>
+hipError_t launch_partition_counts(int b, const PartArgs &pa, hipStream_t s) {
+    const dim3 grid(pa.partitions);
+    switch (b) {
+        case 1: partition_count_kernel<1, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<1><<<1, 256, 0, s>>>(pa); break;
+        case 2: partition_count_kernel<2, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<2><<<1, 256, 0, s>>>(pa); break;
+        case 4: partition_count_kernel<4, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<4><<<1, 256, 0, s>>>(pa); break;
+        default: partition_count_kernel<8, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<8><<<1, 256, 0, s>>>(pa); break;
+    }
+    return hipGetLastError();
 }
 
 template <int B, int KK, int PK>
@@ -381,6 +399,68 @@ bool key_transform(int key_type, int descending, int &kk, uint32_t &flip, uint32
     }
 }
 
+// Reduce-then-scan passes (CUDA Handbook ch.16: count, scan the counts, scatter;
+// 100 Days of GPU, Day 35: persistent blocks walking their tiles in order): per
+// pass, an upsweep counts the digit over each of up to 512 partitions of whole
+// tiles, one workgroup scans those counts into start offsets, and the sweep
+// sorts each partition's tiles in order from them.  No histogram kernel, no
+// look-back; the upsweep reads the keys once more per pass.
+int sort_32_reduce_then_scan(const Plan &p, int kk, uint32_t flip, uint32_t flip_neg, bool pairs,
+                             const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+                             uint32_t *vals_out, uint8_t *ws, hipStream_t s) {
+    const uint64_t part_tiles = cdiv(p.num_tiles, std::min<uint64_t>(p.num_tiles, kPartitions));
+    const uint64_t partitions = cdiv(p.num_tiles, part_tiles);
+    uint32_t *counts = reinterpret_cast<uint32_t *>(ws + p.off_status[0]);  // partitions x R <= tiles x R
+    uint32_t *alt_k = reinterpret_cast<uint32_t *>(ws + p.off_alt_keys);
+    uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
+    const uint32_t *src_k = keys_in;
+    const uint32_t *src_v = vals_in;
+    for (int pass = 0; pass < p.passes; ++pass) {
+        SweepArgs a = pass_args(p, ws, pass);
+        PartArgs pa{};
+        pa.keys = src_k;
+        pa.counts = counts;
+        pa.n = static_cast<uint32_t>(p.row_len);
+        pa.part_len = static_cast<uint32_t>(part_tiles * kTileCfgs[p.tile_cfg].tile);
+        pa.partitions = static_cast<uint32_t>(partitions);
+        pa.shift = a.shift;
+        pa.digit_mask = a.digit_mask;
+        pa.flip = flip;
+        pa.flip_neg = flip_neg;
+        {
+            TimedLaunch t(1, s);
+            const hipError_t e = (kk == kKeyU32) ? launch_partition_counts<kKeyU32>(p.b, pa, s)
+                                                 : launch_partition_counts<kKeyX32>(p.b, pa, s);
+            t.done();
+            if (e != hipSuccess) return LRS_ERR_HIP;
+        }
+        uint32_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
+        a.keys_in = src_k;
+        a.keys_out = dk;
+        a.flip = flip;
+        a.flip_neg = flip_neg;
+        a.part_offsets = counts;
+        a.part_tiles = static_cast<uint32_t>(part_tiles);
+        hipError_t e;
+        TimedLaunch t(2, s);
+        if (pairs) {
+            uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
+            a.vals_in = src_v;
+            a.vals_out = dv;
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s)
+                                : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s);
+            src_v = dv;
+        } else {
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s)
+                                : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s);
+        }
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+        src_k = dk;
+    }
+    return LRS_OK;
+}
+
 // Keys of 32 bits: u32 as they are (KK = kKeyU32), anything else through the
 // two-mask transform (KK = kKeyX32).
 int sort_32(int kk, uint32_t flip, uint32_t flip_neg, bool pairs, const uint32_t *keys_in,
@@ -424,6 +504,8 @@ int sort_32(int kk, uint32_t flip, uint32_t flip_neg, bool pairs, const uint32_t
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
+    if (g_scan_strategy == LRS_SCAN_REDUCE_THEN_SCAN)
+        return sort_32_reduce_then_scan(p, kk, flip, flip_neg, pairs, keys_in, vals_in, keys_out, vals_out, ws, s);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
     if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, s) != hipSuccess)
@@ -632,6 +714,13 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
     hipError_t e = hipGetLastError();
     t.done();
     return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
+int radix_sort_set_scan_strategy(int strategy) {
+    if (strategy != LRS_SCAN_LOOKBACK && strategy != LRS_SCAN_REDUCE_THEN_SCAN) return -1;
+    const int old = g_scan_strategy;
+    g_scan_strategy = strategy;
+    return old;
 }
 
 uint32_t radix_sort_set_spin_limit(uint32_t polls) {

@@ -235,6 +235,12 @@ struct SweepArgs {
     uint32_t flip_neg;
     uint32_t spin_limit;     // polls of an unpublished look-back word before the tile counts
                              // its prefix from the keys; 0: always count from the keys
+    // Reduce-then-scan (partition) mode: workgroup g sorts tiles
+    // [g * part_tiles, (g + 1) * part_tiles) in order, starting digit d at
+    // part_offsets[g * R + d] (the output index of its partition's first key
+    // of digit d).
+    const uint32_t *part_offsets;
+    uint32_t part_tiles;
 };
 
 // Tile handed to the calling workgroup.  The tiles of a pass are dealt to the
@@ -295,8 +301,16 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
 // 5. Publish this tile's inclusive counts, then write the keys (and then the
 //    payload through the same slots) with consecutive threads taking
 //    consecutive slots, so each digit run goes to consecutive addresses.
-template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, int MATCH>
-__global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
+//
+// With PART set (reduce-then-scan) a workgroup instead sorts the consecutive
+// tiles of one partition in order: each tile's digit runs start where the
+// previous tile's ended, from offsets a scan of partition counts computed
+// before the launch, so nothing is published or waited for.
+//
+// At least four waves per SIMD (two 512-thread workgroups per CU): the
+// partition loop would otherwise take 198 registers and halve that.
+template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, int MATCH, bool PART = false>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void sweep_kernel(SweepArgs a) {
     constexpr uint32_t R = 1u << B;
     constexpr int WAVES = BLOCK / kWave;
     constexpr uint32_t TILE = BLOCK * ITEMS;
@@ -323,10 +337,11 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     // 64-bit look-back words also mark rows too long for 32-bit buffer offsets
     constexpr bool kWide = sizeof(W) == 8;
 
+    static_assert(!PART || MATCH == kMatchBallot, "partition mode ranks by ballots");
     for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
     if constexpr (MATCH == kMatchLds)
         for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_match[0][0])[i] = 0ull;
-    if (tid == 0) {
+    if (!PART && tid == 0) {
         s_ticket = take_tile(a.tile_counter, a.num_tiles);
         s_gave_up = 0u;
     }
@@ -334,8 +349,18 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
 
     // Tiles are numbered row-major.  A tile waits below only for earlier tiles
     // of its row, and for a bounded number of polls (see the look-back).
-    const uint32_t t = s_ticket;
-    if (t >= a.num_tiles) return;  // cannot happen with zeroed counters and grid == num_tiles
+    uint32_t t_first, t_end;
+    uint32_t running = 0u;  // partition mode: thread d's output index of the next key of digit d
+    if constexpr (PART) {
+        t_first = blockIdx.x * a.part_tiles;
+        t_end = min(a.num_tiles, t_first + a.part_tiles);
+        if (tid < static_cast<int>(R)) running = a.part_offsets[static_cast<uint64_t>(blockIdx.x) * R + tid];
+    } else {
+        t_first = s_ticket;
+        t_end = t_first + 1u;
+    }
+    if (t_first >= a.num_tiles) return;  // not with zeroed counters and grid == num_tiles
+    for (uint32_t t = t_first; t < t_end; ++t) {
     const uint32_t row = t / a.tiles_per_row;
     const uint32_t tile_in_row = t - row * a.tiles_per_row;
     const uint32_t tile_start = tile_in_row * TILE;
@@ -398,13 +423,16 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     uint32_t real = count;  // padding is not part of the count of the last digit
     if (tid == static_cast<int>(R) - 1) real -= TILE - valid;
     W *status = static_cast<W *>(a.status) + static_cast<uint64_t>(t) * R;
-    if (tid < static_cast<int>(R))
+    if (!PART && tid < static_cast<int>(R))
         publish(status + tid, static_cast<W>((tile_in_row == 0 ? St::kInclusive : St::kAggregate) |
                                              static_cast<W>(real)));
     const uint32_t local_start = block_exclusive_scan_n<BLOCK>(count, s_tmp, lane, wave);
-    const uint32_t hcount = (tid < static_cast<int>(R))
-        ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
-    const uint32_t bucket_base = block_exclusive_scan_n<BLOCK>(hcount, s_tmp, lane, wave);
+    uint32_t bucket_base = 0u;
+    if constexpr (!PART) {
+        const uint32_t hcount = (tid < static_cast<int>(R))
+            ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
+        bucket_base = block_exclusive_scan_n<BLOCK>(hcount, s_tmp, lane, wave);
+    }
     if (tid < static_cast<int>(R)) {
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
@@ -442,7 +470,12 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
     // workgroup counts the digit over the row's keys before this tile instead
     // (the exact exclusive prefix, at the cost of reading them).  So no tile
     // waits forever, whatever order the hardware starts workgroups in.
-    {
+    if constexpr (PART) {
+        if (tid < static_cast<int>(R)) {
+            s_goff[tid] = running - local_start;
+            running += real;
+        }
+    } else {
         W excl = 0;
         const bool from_keys = a.spin_limit == 0u && tile_in_row != 0u;
         bool done = tile_in_row == 0 || from_keys || tid >= static_cast<int>(R);
@@ -553,6 +586,13 @@ __global__ __launch_bounds__(BLOCK) void sweep_kernel(SweepArgs a) {
                 BufIO<OutT>::store(vout_rsrc, dst, s_buf[k]);
             }
         }
+    }
+    if constexpr (PART) {
+        // the next tile reuses the LDS: counters cleared, every read of this tile done
+        __syncthreads();
+        for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
+        __syncthreads();
+    }
     }
 }
 
@@ -817,6 +857,99 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
             if (c) atomicAdd(out + i, c);
         } else {
             out[i] = c;
+        }
+    }
+}
+
+// --------------------------------------------- reduce-then-scan, per pass
+
+struct PartArgs {
+    const void *keys;
+    uint32_t *counts;        // [partitions][R]: this pass's digit counts, then (scan) start offsets
+    uint32_t n;
+    uint32_t part_len;       // elements per partition (whole tiles)
+    uint32_t partitions;
+    uint32_t shift;
+    uint32_t digit_mask;
+    uint32_t flip, flip_neg;
+};
+
+// Upsweep: the pass digit's count over each partition (one workgroup per
+// partition), written without atomics.  Lane copies of the counters as in the
+// histogram kernel.
+template <int B, int KK>
+__global__ __launch_bounds__(kHistBlock) void partition_count_kernel(PartArgs a) {
+    constexpr uint32_t R = 1u << B;
+    constexpr int kCopies = 32;
+    using Stored = typename KeyTraits<KK>::Stored;
+    __shared__ uint32_t s_c[R * kCopies];
+    for (uint32_t i = threadIdx.x; i < R * kCopies; i += kHistBlock) s_c[i] = 0u;
+    __syncthreads();
+    const uint32_t g = blockIdx.x;
+    const uint64_t lo = static_cast<uint64_t>(g) * a.part_len;
+    const uint32_t len = static_cast<uint32_t>(min(static_cast<uint64_t>(a.part_len), a.n - lo));
+    const Stored *keys = static_cast<const Stored *>(a.keys) + lo;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(keys, len * sizeof(Stored));
+    uint32_t *mine = s_c + (threadIdx.x % kCopies);
+    constexpr int kUnroll = 8;
+    for (uint32_t i = threadIdx.x; i < len; i += kUnroll * kHistBlock) {
+        uint32_t v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = BufIO<Stored>::load(rsrc, i + u * kHistBlock);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (i + u * kHistBlock < len) {
+                const uint32_t d = (KeyTraits<KK>::key(v[u], a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
+                atomicAdd(mine + d * kCopies, 1u);
+            }
+    }
+    __syncthreads();
+    for (uint32_t d = threadIdx.x; d < R; d += kHistBlock) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < kCopies; ++k) c += s_c[d * kCopies + ((k + d) % kCopies)];
+        a.counts[static_cast<uint64_t>(g) * R + d] = c;
+    }
+}
+
+// Scan: for each digit, the total over all partitions gives the bucket base
+// (exclusive scan over digits); then each partition's start for the digit is
+// the base plus the counts of the earlier partitions.  One workgroup, thread d
+// owns digit d; counts are replaced by start offsets in place.
+template <int B>
+__global__ __launch_bounds__(256) void partition_scan_kernel(PartArgs a) {
+    constexpr uint32_t R = 1u << B;
+    __shared__ uint32_t s_tmp[256 / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    // Both walks go in batches of kBatch partitions, so each round trip to
+    // memory carries kBatch loads (in the second walk a store to one batch
+    // would otherwise wait for before every load of the next).
+    constexpr uint32_t kBatch = 64;
+    uint32_t total = 0u;
+    if (tid < static_cast<int>(R)) {
+        for (uint32_t g0 = 0; g0 < a.partitions; g0 += kBatch) {
+            uint32_t c[kBatch];
+#pragma unroll
+            for (uint32_t i = 0; i < kBatch; ++i)
+                c[i] = (g0 + i < a.partitions) ? a.counts[static_cast<uint64_t>(g0 + i) * R + tid] : 0u;
+#pragma unroll
+            for (uint32_t i = 0; i < kBatch; ++i) total += c[i];
+        }
+    }
+    uint32_t running = block_exclusive_scan_n<256>(total, s_tmp, lane, wave);
+    if (tid < static_cast<int>(R)) {
+        for (uint32_t g0 = 0; g0 < a.partitions; g0 += kBatch) {
+            uint32_t c[kBatch];
+#pragma unroll
+            for (uint32_t i = 0; i < kBatch; ++i)
+                c[i] = (g0 + i < a.partitions) ? a.counts[static_cast<uint64_t>(g0 + i) * R + tid] : 0u;
+#pragma unroll
+            for (uint32_t i = 0; i < kBatch; ++i) {
+                if (g0 + i < a.partitions) a.counts[static_cast<uint64_t>(g0 + i) * R + tid] = running;
+                running += c[i];
+            }
         }
     }
 }

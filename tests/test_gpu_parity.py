@@ -351,6 +351,52 @@ def test_prefix_counted_from_keys_large_tiles(spin_limit):
     assert_same(gv, ev, "values")
 
 
+# ------------------------------------------------ reduce-then-scan strategy
+
+@pytest.fixture
+def reduce_then_scan():
+    old = lrs.radix_sort_set_scan_strategy("reduce-then-scan")
+    yield
+    lrs.radix_sort_set_scan_strategy(old)
+
+
+@pytest.mark.parametrize("n", [8193, 300_001, 3_000_017, 15_000_007])
+def test_reduce_then_scan_strategy(n, reduce_then_scan):
+    # every tile shape; partitions of one tile (small n) and of several (15M)
+    keys = workloads.random_u32(9400 + n % 1000, n)
+    if n == 3_000_017:
+        keys &= workloads.random_u32(9401, n) & workloads.random_u32(9402, n)
+    vals = np.arange(n, dtype=np.uint32)
+    for b, begin, end in ((8, 0, 32), (4, 0, 32)) if n > 300_001 else ((8, 0, 32), (4, 3, 30), (1, 0, 5), (2, 7, 18)):
+        log(f"reduce-then-scan n={n} b={b} bits [{begin},{end})")
+        ek, ev = oracle.radix_sort_pairs(keys, vals, begin, end, b)
+        gk, gv = gpu_pairs(keys, vals, begin, end, b)
+        assert_same(gk, ek, "keys")
+        assert_same(gv, ev, "values")
+        assert_same(gpu_keys(keys, begin, end, b), ek, "keys only")
+
+
+def test_reduce_then_scan_typed_keys(reduce_then_scan):
+    n = 1_000_003
+    bits = workloads.normal_f64(9500, n).astype(np.float32)
+    bits[::7] = np.round(bits[::7])
+    kt = torch.from_numpy(bits.copy()).cuda()
+    vals = np.arange(n, dtype=np.uint32)
+    vt = to_gpu(vals)
+    for desc in (False, True):
+        ko, vo = lrs.radix_sort_pairs_typed(kt, vt, desc)
+        torch.cuda.synchronize()
+        ek, ev = oracle.radix_sort_typed(bits.view(np.uint32), vals, "f32", desc)
+        assert_same(ko.view(torch.int32).cpu().numpy().view(np.uint32), ek, f"f32 desc={desc} keys")
+        assert_same(to_np_u32(vo), ev, f"f32 desc={desc} values")
+
+
+def test_scan_strategy_rejects_unknown():
+    lib = lrs.load_library()
+    assert lib.radix_sort_set_scan_strategy(7) == -1
+    assert lrs.radix_sort_set_scan_strategy("lookback") in ("lookback", "reduce-then-scan")
+
+
 # ------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("n", [1000, 300_000])
