@@ -71,16 +71,20 @@ WORKLOADS = {
                                      "descending, 8-bit digits, 4 passes"),
     "i32_keys_2p28_asc": dict(kind="keys", typed="i32", descending=False, n=1 << 28, end_bit=32, b=8,
                               desc="2^28 uniform int32 keys, keys only, ascending, 8-bit digits, 4 passes"),
+    "f64_pairs_2p27_asc": dict(kind="pairs", typed="f64", descending=False, n=1 << 27, end_bit=64, b=8,
+                               key_bytes=8, desc="2^27 fp64 N(0,1) keys + u32 value pairs (value = original "
+                                                 "index), ascending, 8-bit digits, 8 passes"),
 }
 
 
 def sweep_bytes(w) -> int:
     """Algorithmic bytes of all sweep launches of one sort of workload w."""
     P = -(-w["end_bit"] // w["b"]) if w["kind"] != "rows" else 16 // w["b"]
+    kb = w.get("key_bytes", 4)
     if w["kind"] == "keys":
-        return 8 * w["n"] * P
+        return 2 * kb * w["n"] * P
     if w["kind"] == "pairs":
-        return 16 * w["n"] * P
+        return (2 * kb + 8) * w["n"] * P
     n = w["rows"] * w["cols"]
     total = 0
     for p in range(P):
@@ -181,18 +185,23 @@ def main():
         scratch = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
         copy_pair = (scratch[: 1 << 27], scratch[1 << 27:])
     elif w["kind"] == "pairs" and "typed" in w:
-        keys = workloads.keys_f32_normal(w["n"])
-        k_in = torch.from_numpy(keys.view(np.int32)).to(dev).view(torch.float32)
+        if w["typed"] == "f64":
+            keys = workloads.keys_f64_normal(w["n"])
+            k_in = torch.from_numpy(keys.view(np.int64)).to(dev).view(torch.float64)
+        else:
+            keys = workloads.keys_f32_normal(w["n"])
+            k_in = torch.from_numpy(keys.view(np.int32)).to(dev).view(torch.float32)
         del keys
         v_in = torch.arange(w["n"], dtype=torch.int32, device=dev)
         n_keys = w["n"]
         k_out = torch.empty_like(k_in)
         v_out = torch.empty_like(v_in)
-        ws = torch.empty(lrs.radix_sort_workspace_size(n_keys, 0, 32, w["b"], True), dtype=torch.uint8, device=dev)
+        ws = torch.empty(lrs.radix_sort_typed_workspace_size(n_keys, w["typed"], 0, w["end_bit"], w["b"], True),
+                         dtype=torch.uint8, device=dev)
 
         def step():
-            lrs.radix_sort_pairs_typed(k_in, v_in, w["descending"], w["typed"], 0, 32, w["b"], keys_out=k_out,
-                                       values_out=v_out, workspace=ws)
+            lrs.radix_sort_pairs_typed(k_in, v_in, w["descending"], w["typed"], 0, w["end_bit"], w["b"],
+                                       keys_out=k_out, values_out=v_out, workspace=ws)
         copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
     elif w["kind"] == "pairs":
         keys, vals = workloads.pairs_c3(w["n"], w["dist"])
@@ -277,7 +286,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16" if w["kind"] == "rows" else "u32",
+        "dtype": "u16" if w["kind"] == "rows" else ("u64" if w.get("key_bytes", 4) == 8 else "u32"),
         "data": "synthetic",
         "config": {"workload": w["desc"], "name": name, "n": n_keys, "digit_bits": w["b"],
                    "passes": launches_per_sort, "scan": args.scan},

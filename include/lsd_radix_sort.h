@@ -58,10 +58,13 @@ typedef enum lrs_status {
 #define LRS_DTYPE_FP16 0
 #define LRS_DTYPE_BF16 1
 
-/* 32-bit key types of radix_sort_keys_typed / radix_sort_pairs_typed. */
+/* Key types of radix_sort_keys_typed / radix_sort_pairs_typed. */
 #define LRS_KEY_U32 0
 #define LRS_KEY_I32 1
 #define LRS_KEY_F32 2
+#define LRS_KEY_U64 3
+#define LRS_KEY_I64 4
+#define LRS_KEY_F64 5
 
 /* Largest u32 sort: n < 2^32 elements.  Largest segmented row: n < 2^30
  * (FlagTree PR #1084 caps one row at 2^30 elements). */
@@ -101,25 +104,32 @@ int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t 
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Stable LSD sort of n 32-bit keys of type key_type, ascending or descending,
- * with or without a u32 payload.  The sort orders the key's order-preserving
- * u32 image (100 Days of GPU, Day 35, "Pitfalls": a bijection on the way in,
- * so floats and signed integers sort as unsigned integers):
- *   LRS_KEY_U32  the value itself;
- *   LRS_KEY_I32  two's complement with the sign bit flipped;
- *   LRS_KEY_F32  IEEE-754 binary32 bits: negative patterns complemented,
- *                non-negative ones with the sign bit set.  So -0 sorts
- *                immediately before +0, and NaNs sort by bit pattern beyond
- *                the infinities (sign-bit-set NaNs first, the others last);
+ * Stable LSD sort of n 32- or 64-bit keys of type key_type, ascending or
+ * descending, with or without a u32 payload.  The sort orders the key's
+ * order-preserving unsigned image (100 Days of GPU, Day 35, "Pitfalls": a
+ * bijection on the way in, so floats and signed integers sort as unsigned
+ * integers):
+ *   LRS_KEY_U32 / U64  the value itself;
+ *   LRS_KEY_I32 / I64  two's complement with the sign bit flipped;
+ *   LRS_KEY_F32 / F64  IEEE-754 binary32 / binary64 bits: negative patterns
+ *                complemented, non-negative ones with the sign bit set.  So
+ *                -0 sorts immediately before +0, and NaNs sort by bit pattern
+ *                beyond the infinities (sign-bit-set NaNs first, the others last);
  * descending (nonzero) sorts the complement of that image, so equal keys keep
  * their input order in both directions.  [begin_bit, end_bit) selects bits of
- * the image (0, 32 for a full sort).  The stored key bits are what is moved;
- * the outputs hold input values, never transformed ones.  Pointers, sizes,
- * workspace (radix_sort_workspace_size with the same arguments), alignment and
- * errors are as for radix_sort_keys / radix_sort_pairs; an unknown key_type
+ * the image (0, 32 or 0, 64 for a full sort; end_bit <= the key width).  The
+ * stored key bits are what is moved; the outputs hold input values, never
+ * transformed ones.  Keys are 4-byte (32-bit types) or 8-byte (64-bit types)
+ * elements, aligned to their size; the workspace size comes from
+ * radix_sort_typed_workspace_size (for 32-bit types it equals
+ * radix_sort_workspace_size).  Pointers, sizes, alignment and errors are
+ * otherwise as for radix_sort_keys / radix_sort_pairs; an unknown key_type
  * returns LRS_ERR_DTYPE.  LRS_KEY_U32 ascending is exactly radix_sort_keys /
- * radix_sort_pairs.
+ * radix_sort_pairs.  64-bit keys always take the multi-launch path (no
+ * whole-row resident sort) and the look-back scan strategy.
  */
+size_t radix_sort_typed_workspace_size(uint64_t n, int key_type, int begin_bit, int end_bit, int digit_bits,
+                                       int with_values);
 int radix_sort_keys_typed(const void *keys_in, void *keys_out, uint64_t n, int key_type, int descending,
                           int begin_bit, int end_bit, int digit_bits, void *workspace,
                           size_t workspace_bytes, void *stream);

@@ -31,6 +31,9 @@ LRS_DTYPE_BF16 = 1
 LRS_KEY_U32 = 0
 LRS_KEY_I32 = 1
 LRS_KEY_F32 = 2
+LRS_KEY_U64 = 3
+LRS_KEY_I64 = 4
+LRS_KEY_F64 = 5
 LRS_SCAN_LOOKBACK = 0
 LRS_SCAN_REDUCE_THEN_SCAN = 1
 _SCAN_STRATEGIES = {"lookback": LRS_SCAN_LOOKBACK, "reduce-then-scan": LRS_SCAN_REDUCE_THEN_SCAN}
@@ -77,6 +80,8 @@ def load_library():
     lib.radix_sort_digit_histograms.restype = c_int
     lib.radix_sort_copy_probe.argtypes = [P, P, szt, P]
     lib.radix_sort_copy_probe.restype = c_int
+    lib.radix_sort_typed_workspace_size.argtypes = [u64, c_int, c_int, c_int, c_int, c_int]
+    lib.radix_sort_typed_workspace_size.restype = szt
     lib.radix_sort_keys_typed.argtypes = [P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
     lib.radix_sort_keys_typed.restype = c_int
     lib.radix_sort_pairs_typed.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
@@ -174,34 +179,50 @@ def radix_sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 
     return keys_out, values_out
 
 
-_KEY_TYPES = {"u32": LRS_KEY_U32, "i32": LRS_KEY_I32, "f32": LRS_KEY_F32}
-_KEY_DTYPES = {torch.uint32: "u32", torch.int32: "i32", torch.float32: "f32"}
+_KEY_TYPES = {"u32": LRS_KEY_U32, "i32": LRS_KEY_I32, "f32": LRS_KEY_F32,
+              "u64": LRS_KEY_U64, "i64": LRS_KEY_I64, "f64": LRS_KEY_F64}
+_KEY_DTYPES = {torch.uint32: "u32", torch.int32: "i32", torch.float32: "f32",
+               torch.uint64: "u64", torch.int64: "i64", torch.float64: "f64"}
 
 
 def _typed_keys(keys: torch.Tensor, key_type: str | None):
     if not isinstance(keys, torch.Tensor) or not keys.is_cuda:
         raise ValueError("keys must be a GPU tensor")
     if keys.dtype not in _KEY_DTYPES:
-        raise ValueError(f"keys must be uint32, int32 or float32, got {keys.dtype}")
+        raise ValueError(f"keys must be a 32- or 64-bit integer or float tensor, got {keys.dtype}")
     if keys.dim() != 1 or not keys.is_contiguous():
         raise ValueError("keys must be a contiguous 1-D tensor")
     kt = _KEY_DTYPES[keys.dtype] if key_type is None else key_type
     if kt not in _KEY_TYPES:
         raise ValueError(f"key_type must be one of {sorted(_KEY_TYPES)}")
+    if (kt.endswith("64")) != (keys.element_size() == 8):
+        raise ValueError(f"key_type {kt} does not match a {keys.element_size() * 8}-bit tensor")
     return _KEY_TYPES[kt]
 
 
+def radix_sort_typed_workspace_size(n: int, key_type: str, begin_bit: int = 0, end_bit: int | None = None,
+                                    digit_bits: int = 8, with_values: bool = False) -> int:
+    if end_bit is None:
+        end_bit = 64 if key_type.endswith("64") else 32
+    return int(load_library().radix_sort_typed_workspace_size(n, _KEY_TYPES[key_type], begin_bit, end_bit,
+                                                              digit_bits, int(with_values)))
+
+
 def radix_sort_keys_typed(keys: torch.Tensor, descending: bool = False, key_type: str | None = None,
-                          begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8,
+                          begin_bit: int = 0, end_bit: int | None = None, digit_bits: int = 8,
                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Stable sort of 32-bit keys as u32, i32 or f32 (from the dtype unless key_type is given)."""
+    """Stable sort of 32- or 64-bit keys as unsigned, signed or float (from the dtype
+    unless key_type is given); end_bit defaults to the key width."""
     lib = load_library()
     kt = _typed_keys(keys, key_type)
+    if end_bit is None:
+        end_bit = 8 * keys.element_size()
     n = keys.numel()
     if out is None:
         out = torch.empty_like(keys)
     if workspace is None:
-        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 0), keys.device)
+        workspace = _workspace(lib.radix_sort_typed_workspace_size(n, kt, begin_bit, end_bit, digit_bits, 0),
+                               keys.device)
     _check(lib.radix_sort_keys_typed(_ptr(keys), _ptr(out), n, kt, int(descending), begin_bit, end_bit,
                                      digit_bits, _ptr(workspace), workspace.numel(), _stream(keys)),
            "radix_sort_keys_typed")
@@ -209,12 +230,14 @@ def radix_sort_keys_typed(keys: torch.Tensor, descending: bool = False, key_type
 
 
 def radix_sort_pairs_typed(keys: torch.Tensor, values: torch.Tensor, descending: bool = False,
-                           key_type: str | None = None, begin_bit: int = 0, end_bit: int = 32,
+                           key_type: str | None = None, begin_bit: int = 0, end_bit: int | None = None,
                            digit_bits: int = 8, keys_out: torch.Tensor | None = None,
                            values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """As radix_sort_keys_typed, carrying one 32-bit payload per key; returns (keys, values)."""
     lib = load_library()
     kt = _typed_keys(keys, key_type)
+    if end_bit is None:
+        end_bit = 8 * keys.element_size()
     values = _u32_tensor(values, "values")
     n = keys.numel()
     if values.numel() != n:
@@ -224,7 +247,8 @@ def radix_sort_pairs_typed(keys: torch.Tensor, values: torch.Tensor, descending:
     if values_out is None:
         values_out = torch.empty_like(values)
     if workspace is None:
-        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 1), keys.device)
+        workspace = _workspace(lib.radix_sort_typed_workspace_size(n, kt, begin_bit, end_bit, digit_bits, 1),
+                               keys.device)
     _check(lib.radix_sort_pairs_typed(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, kt,
                                       int(descending), begin_bit, end_bit, digit_bits, _ptr(workspace),
                                       workspace.numel(), _stream(keys)), "radix_sort_pairs_typed")

@@ -32,6 +32,9 @@ struct TileCfg {
 };
 constexpr TileCfg kTileCfgs[3] = {
     {256, 16, 4096}, {512, 16, 8192}, {kSweepBlock, LRS_SWEEP_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_ITEMS}};
+// 64-bit keys take twice the registers and LDS per key: half the keys per tile.
+constexpr TileCfg kTileCfgs64[3] = {{256, 8, 2048}, {512, 8, 4096}, {512, 16, 8192}};
+constexpr TileCfg tile_cfg_of(bool key64, int c) { return key64 ? kTileCfgs64[c] : kTileCfgs[c]; }
 #ifndef LRS_MIN_TILES
 #define LRS_MIN_TILES 256
 #endif
@@ -44,9 +47,9 @@ constexpr uint64_t kResidentMax = 8192;
 // The largest tile shape with at least kMinTiles tiles and at most 1/32 of
 // its elements past row ends (rows of 65536 take eight 8192-key tiles, not
 // five 15360-key tiles with 15% padding).
-int choose_tile_cfg(uint64_t rows, uint64_t row_len) {
+int choose_tile_cfg(uint64_t rows, uint64_t row_len, bool key64) {
     for (int c = 2; c >= 1; --c) {
-        const uint64_t tile = kTileCfgs[c].tile;
+        const uint64_t tile = tile_cfg_of(key64, c).tile;
         const uint64_t tiles = rows * ((row_len + tile - 1) / tile);
         const uint64_t padded = tiles * tile;
         if (tiles >= kMinTiles && (padded - rows * row_len) * 32 <= padded) return c;
@@ -145,8 +148,10 @@ struct Plan {
 };
 
 // kind: 0 keys, 1 pairs, 2 segmented
-Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int b, int kind) {
+// kind: 0 keys, 1 pairs, 2 segmented; key_bytes: 4 or 8 (segmented keys are 2 bytes)
+Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int b, int kind, int key_bytes = 4) {
     Plan p;
+    const bool key64 = key_bytes == 8;
     p.rows = rows;
     p.row_len = row_len;
     p.b = b;
@@ -154,8 +159,8 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.end_bit = end_bit;
     p.passes = static_cast<int>(cdiv(static_cast<uint64_t>(end_bit - begin_bit), b));
     const uint64_t R = 1ull << b;
-    p.tile_cfg = choose_tile_cfg(rows, row_len);
-    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, kTileCfgs[p.tile_cfg].tile));
+    p.tile_cfg = choose_tile_cfg(rows, row_len, key64);
+    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, tile_cfg_of(key64, p.tile_cfg).tile));
     p.num_tiles = rows * p.tiles_per_row;
     p.wide_status = row_len >= (1ull << 29);
 
@@ -164,7 +169,7 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.hist_chunks_per_row = static_cast<uint32_t>(std::max<uint64_t>(
         1, std::min<uint64_t>(cdiv(row_len, kHistMinChunk), cdiv(kHistTargetBlocks, rows))));
 
-    const uint64_t keysz = (kind == 2) ? 2 : 4;
+    const uint64_t keysz = (kind == 2) ? 2 : static_cast<uint64_t>(key_bytes);
     const uint64_t n = rows * row_len;
     uint64_t off = 0;
     p.off_hist = off;
@@ -196,7 +201,7 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
         }
     }
     p.total = off;
-    if (row_len <= kResidentMax) {
+    if (row_len <= kResidentMax && !key64) {
         p.resident = true;
         p.total = 0;
     }
@@ -257,16 +262,18 @@ void launch_sweep_cfg(const SweepArgs &a, uint64_t grid_size, hipStream_t s) {
 
 template <int B, int KK, int PK, bool PART>
 hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s) {
+    constexpr bool k64 = sizeof(typename KeyTraits<KK>::Stored) == 8;
+    constexpr TileCfg c0 = tile_cfg_of(k64, 0), c1 = tile_cfg_of(k64, 1), c2 = tile_cfg_of(k64, 2);
     // 64-bit look-back words (and 64-bit store addressing) only occur for rows
     // of 2^29 or more elements, which always take the largest tile.
     if (wide)
-        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint64_t, PART>(a, grid, s);
+        launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint64_t, PART>(a, grid, s);
     else if (cfg == 2)
-        launch_sweep_cfg<B, kTileCfgs[2].items, kTileCfgs[2].block, KK, PK, uint32_t, PART>(a, grid, s);
+        launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint32_t, PART>(a, grid, s);
     else if (cfg == 1)
-        launch_sweep_cfg<B, kTileCfgs[1].items, kTileCfgs[1].block, KK, PK, uint32_t, PART>(a, grid, s);
+        launch_sweep_cfg<B, c1.items, c1.block, KK, PK, uint32_t, PART>(a, grid, s);
     else
-        launch_sweep_cfg<B, kTileCfgs[0].items, kTileCfgs[0].block, KK, PK, uint32_t, PART>(a, grid, s);
+        launch_sweep_cfg<B, c0.items, c0.block, KK, PK, uint32_t, PART>(a, grid, s);
     return hipGetLastError();
 }
 
@@ -336,7 +343,7 @@ hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, hipStream_t 
     return e;
 }
 
-hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint32_t flip, uint32_t flip_neg,
+hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint64_t flip, uint64_t flip_neg,
                             bool accumulate, hipStream_t s) {
     HistArgs h{};
     h.keys = keys;
@@ -353,6 +360,8 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     TimedLaunch t(1, s);
     hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, static_cast<uint32_t>(blocks), s)
                    : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, static_cast<uint32_t>(blocks), s)
+                   : (kk == kKeyU64) ? launch_hist<kKeyU64>(p.b, h, static_cast<uint32_t>(blocks), s)
+                   : (kk == kKeyX64) ? launch_hist<kKeyX64>(p.b, h, static_cast<uint32_t>(blocks), s)
                                      : launch_hist<kKeyF16>(p.b, h, static_cast<uint32_t>(blocks), s);
     t.done();
     return e;
@@ -389,14 +398,23 @@ T *pass_dst(int pass, int passes, T *out, T *alt) {
 // Kernel key kind and transform masks of a (key type, direction); false for an
 // unknown key type.  The masks give each type's order-preserving u32 image and
 // complement it for descending order (see KeyTraits<kKeyX32>).
-bool key_transform(int key_type, int descending, int &kk, uint32_t &flip, uint32_t &flip_neg) {
-    const uint32_t c = descending ? 0xFFFFFFFFu : 0u;
+bool key_transform(int key_type, int descending, int &kk, uint64_t &flip, uint64_t &flip_neg) {
+    const uint64_t c = descending ? ~0ull : 0ull;
+    const uint64_t c32 = c & 0xFFFFFFFFull;
+    const uint64_t top64 = 1ull << 63;
     switch (key_type) {
-        case LRS_KEY_U32: kk = descending ? kKeyX32 : kKeyU32; flip = c; flip_neg = c; return true;
-        case LRS_KEY_I32: kk = kKeyX32; flip = 0x80000000u ^ c; flip_neg = 0x80000000u ^ c; return true;
-        case LRS_KEY_F32: kk = kKeyX32; flip = 0x80000000u ^ c; flip_neg = 0xFFFFFFFFu ^ c; return true;
+        case LRS_KEY_U32: kk = descending ? kKeyX32 : kKeyU32; flip = c32; flip_neg = c32; return true;
+        case LRS_KEY_I32: kk = kKeyX32; flip = 0x80000000ull ^ c32; flip_neg = 0x80000000ull ^ c32; return true;
+        case LRS_KEY_F32: kk = kKeyX32; flip = 0x80000000ull ^ c32; flip_neg = 0xFFFFFFFFull ^ c32; return true;
+        case LRS_KEY_U64: kk = descending ? kKeyX64 : kKeyU64; flip = c; flip_neg = c; return true;
+        case LRS_KEY_I64: kk = kKeyX64; flip = top64 ^ c; flip_neg = top64 ^ c; return true;
+        case LRS_KEY_F64: kk = kKeyX64; flip = top64 ^ c; flip_neg = ~0ull ^ c; return true;
         default: return false;
     }
+}
+
+bool key_type_is_64(int key_type) {
+    return key_type == LRS_KEY_U64 || key_type == LRS_KEY_I64 || key_type == LRS_KEY_F64;
 }
 
 // Reduce-then-scan passes (CUDA Handbook ch.16: count, scan the counts, scatter;
@@ -405,7 +423,7 @@ bool key_transform(int key_type, int descending, int &kk, uint32_t &flip, uint32
 // tiles, one workgroup scans those counts into start offsets, and the sweep
 // sorts each partition's tiles in order from them.  No histogram kernel, no
 // look-back; the upsweep reads the keys once more per pass.
-int sort_32_reduce_then_scan(const Plan &p, int kk, uint32_t flip, uint32_t flip_neg, bool pairs,
+int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip_neg, bool pairs,
                              const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
                              uint32_t *vals_out, uint8_t *ws, hipStream_t s) {
     const uint64_t part_tiles = cdiv(p.num_tiles, std::min<uint64_t>(p.num_tiles, kPartitions));
@@ -421,7 +439,7 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint32_t flip, uint32_t flip
         pa.keys = src_k;
         pa.counts = counts;
         pa.n = static_cast<uint32_t>(p.row_len);
-        pa.part_len = static_cast<uint32_t>(part_tiles * kTileCfgs[p.tile_cfg].tile);
+        pa.part_len = static_cast<uint32_t>(part_tiles * tile_cfg_of(false, p.tile_cfg).tile);
         pa.partitions = static_cast<uint32_t>(partitions);
         pa.shift = a.shift;
         pa.digit_mask = a.digit_mask;
@@ -463,7 +481,7 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint32_t flip, uint32_t flip
 
 // Keys of 32 bits: u32 as they are (KK = kKeyU32), anything else through the
 // two-mask transform (KK = kKeyX32).
-int sort_32(int kk, uint32_t flip, uint32_t flip_neg, bool pairs, const uint32_t *keys_in,
+int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t *keys_in,
             const uint32_t *vals_in, uint32_t *keys_out, uint32_t *vals_out, uint64_t n, int begin_bit,
             int end_bit, int b, void *workspace, size_t ws_bytes, void *stream) {
     if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
@@ -542,6 +560,66 @@ int sort_32(int kk, uint32_t flip, uint32_t flip_neg, bool pairs, const uint32_t
     return LRS_OK;
 }
 
+// Keys of 64 bits (u64 as they are, anything else through the two-mask
+// transform): the look-back path with 64-bit tile shapes; no whole-row
+// resident sort and no reduce-then-scan.
+int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t *keys_in,
+            const uint32_t *vals_in, uint64_t *keys_out, uint32_t *vals_out, uint64_t n, int begin_bit,
+            int end_bit, int b, void *workspace, size_t ws_bytes, void *stream) {
+    if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
+    if (begin_bit < 0 || end_bit > 64 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
+    if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
+    if (n == 0) return LRS_OK;
+    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0, 8);
+    if (!keys_in || !keys_out || (pairs && (!vals_in || !vals_out)) || !workspace) return LRS_ERR_NULL_POINTER;
+    if (misaligned(keys_in, 8) || misaligned(keys_out, 8) || misaligned(workspace, 256) ||
+        (pairs && (misaligned(vals_in, 4) || misaligned(vals_out, 4))))
+        return LRS_ERR_ALIGNMENT;
+    if (ws_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
+    const uint64_t kb = 8 * n, vb = 4 * n;
+    if (overlaps(keys_out, kb, keys_in, kb) || overlaps(keys_out, kb, workspace, p.total) ||
+        (pairs && (overlaps(vals_out, vb, vals_in, vb) || overlaps(vals_out, vb, keys_in, kb) ||
+                   overlaps(keys_out, kb, vals_in, vb) || overlaps(vals_out, vb, keys_out, kb) ||
+                   overlaps(vals_out, vb, workspace, p.total))))
+        return LRS_ERR_ALIASING;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, s) != hipSuccess)
+        return LRS_ERR_HIP;
+    uint64_t *alt_k = reinterpret_cast<uint64_t *>(ws + p.off_alt_keys);
+    uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
+    const uint64_t *src_k = keys_in;
+    const uint32_t *src_v = vals_in;
+    for (int pass = 0; pass < p.passes; ++pass) {
+        SweepArgs a = pass_args(p, ws, pass);
+        uint64_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
+        a.keys_in = src_k;
+        a.keys_out = dk;
+        a.flip = flip;
+        a.flip_neg = flip_neg;
+        hipError_t e;
+        TimedLaunch t(2, s);
+        if (pairs) {
+            uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
+            a.vals_in = src_v;
+            a.vals_out = dv;
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX64, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            src_v = dv;
+        } else {
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX64, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+        }
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+        src_k = dk;
+    }
+    return LRS_OK;
+}
+
 }  // namespace
 }  // namespace lrs
 
@@ -571,12 +649,29 @@ int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t 
                    digit_bits, workspace, workspace_bytes, stream);
 }
 
+size_t radix_sort_typed_workspace_size(uint64_t n, int key_type, int begin_bit, int end_bit, int digit_bits,
+                                       int with_values) {
+    int kk;
+    uint64_t flip, flip_neg;
+    if (!key_transform(key_type, 0, kk, flip, flip_neg)) return 0;
+    const int key_bits = key_type_is_64(key_type) ? 64 : 32;
+    if (!digit_bits_ok(digit_bits) || begin_bit < 0 || end_bit > key_bits || begin_bit >= end_bit || n == 0 ||
+        n > LRS_MAX_KEYS)
+        return 0;
+    return static_cast<size_t>(
+        make_plan(1, n, begin_bit, end_bit, digit_bits, with_values ? 1 : 0, key_bits / 8).total);
+}
+
 int radix_sort_keys_typed(const void *keys_in, void *keys_out, uint64_t n, int key_type, int descending,
                           int begin_bit, int end_bit, int digit_bits, void *workspace,
                           size_t workspace_bytes, void *stream) {
     int kk;
-    uint32_t flip, flip_neg;
+    uint64_t flip, flip_neg;
     if (!key_transform(key_type, descending, kk, flip, flip_neg)) return LRS_ERR_DTYPE;
+    if (key_type_is_64(key_type))
+        return sort_64(kk, flip, flip_neg, false, static_cast<const uint64_t *>(keys_in), nullptr,
+                       static_cast<uint64_t *>(keys_out), nullptr, n, begin_bit, end_bit, digit_bits, workspace,
+                       workspace_bytes, stream);
     return sort_32(kk, flip, flip_neg, false, static_cast<const uint32_t *>(keys_in), nullptr,
                    static_cast<uint32_t *>(keys_out), nullptr, n, begin_bit, end_bit, digit_bits, workspace,
                    workspace_bytes, stream);
@@ -586,8 +681,12 @@ int radix_sort_pairs_typed(const void *keys_in, const uint32_t *vals_in, void *k
                            uint64_t n, int key_type, int descending, int begin_bit, int end_bit,
                            int digit_bits, void *workspace, size_t workspace_bytes, void *stream) {
     int kk;
-    uint32_t flip, flip_neg;
+    uint64_t flip, flip_neg;
     if (!key_transform(key_type, descending, kk, flip, flip_neg)) return LRS_ERR_DTYPE;
+    if (key_type_is_64(key_type))
+        return sort_64(kk, flip, flip_neg, true, static_cast<const uint64_t *>(keys_in), vals_in,
+                       static_cast<uint64_t *>(keys_out), vals_out, n, begin_bit, end_bit, digit_bits, workspace,
+                       workspace_bytes, stream);
     return sort_32(kk, flip, flip_neg, true, static_cast<const uint32_t *>(keys_in), vals_in,
                    static_cast<uint32_t *>(keys_out), vals_out, n, begin_bit, end_bit, digit_bits, workspace,
                    workspace_bytes, stream);

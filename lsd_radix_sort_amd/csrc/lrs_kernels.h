@@ -49,7 +49,7 @@ constexpr uint32_t kXcdChunk = LRS_XCD_CHUNK;
 constexpr uint32_t kXcds = 8;          // accelerator complex dies (XCDs) of an MI355X
 constexpr int kWave = 64;              // CDNA wavefront width
 
-enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1, kKeyX32 = 2 };
+enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1, kKeyX32 = 2, kKeyU64 = 3, kKeyX64 = 4 };
 
 // Payload handling of one pass.
 enum PayKind : int {
@@ -64,35 +64,63 @@ enum PayKind : int {
 template <int KK> struct KeyTraits;
 
 // key(v, flip, flip_neg) maps a stored pattern to the unsigned integer whose
-// ascending order is the wanted order.
+// ascending order is the wanted order.  Word is the register type of a key
+// (and of its slot in LDS); the masks are 64-bit, of which 16- and 32-bit keys
+// use the low half.
 
 template <> struct KeyTraits<kKeyU32> {
     using Stored = uint32_t;
+    using Word = uint32_t;
     // The sort key of a stored u32 is the value itself.
-    __device__ static inline uint32_t key(uint32_t v, uint32_t, uint32_t) { return v; }
+    __device__ static inline uint32_t key(uint32_t v, uint64_t, uint64_t) { return v; }
 };
 
 template <> struct KeyTraits<kKeyF16> {
     using Stored = uint16_t;
+    using Word = uint32_t;
     // Order-preserving key of a 16-bit float pattern: complement negatives,
     // set the sign bit of non-negatives; `flip` = 0xFFFF complements the result
     // for descending order.
-    __device__ static inline uint32_t key(uint32_t v, uint32_t flip, uint32_t) {
+    __device__ static inline uint32_t key(uint32_t v, uint64_t flip, uint64_t) {
         uint32_t asc = v ^ ((v & 0x8000u) ? 0xFFFFu : 0x8000u);
-        return asc ^ flip;
+        return asc ^ static_cast<uint32_t>(flip);
     }
 };
 
 template <> struct KeyTraits<kKeyX32> {
     using Stored = uint32_t;
+    using Word = uint32_t;
     // Any other 32-bit key: XOR with `flip` when the sign bit is clear and with
     // `flip_neg` when it is set.  Signed integers: both 0x80000000.  Floats:
     // 0x80000000 and 0xFFFFFFFF (set the sign bit of non-negatives, complement
     // negatives).  Descending order complements both masks (u32: both ~0).
-    __device__ static inline uint32_t key(uint32_t v, uint32_t flip, uint32_t flip_neg) {
-        return v ^ ((static_cast<int32_t>(v) < 0) ? flip_neg : flip);
+    __device__ static inline uint32_t key(uint32_t v, uint64_t flip, uint64_t flip_neg) {
+        return v ^ static_cast<uint32_t>((static_cast<int32_t>(v) < 0) ? flip_neg : flip);
     }
 };
+
+template <> struct KeyTraits<kKeyU64> {
+    using Stored = uint64_t;
+    using Word = uint64_t;
+    __device__ static inline uint64_t key(uint64_t v, uint64_t, uint64_t) { return v; }
+};
+
+template <> struct KeyTraits<kKeyX64> {
+    using Stored = uint64_t;
+    using Word = uint64_t;
+    // As kKeyX32 with 64-bit masks (signed integers: both 2^63; doubles: 2^63
+    // and ~0; complemented for descending order).
+    __device__ static inline uint64_t key(uint64_t v, uint64_t flip, uint64_t flip_neg) {
+        return v ^ ((static_cast<int64_t>(v) < 0) ? flip_neg : flip);
+    }
+};
+
+// The pass digit of a key word: `mask` bits from bit `shift` of its key.
+template <int KK>
+__device__ inline uint32_t digit_of(typename KeyTraits<KK>::Word v, uint64_t flip, uint64_t flip_neg,
+                                    uint32_t shift, uint32_t mask) {
+    return static_cast<uint32_t>(KeyTraits<KK>::key(v, flip, flip_neg) >> shift) & mask;
+}
 
 // Range-checked buffer access: a load past the resource's byte count returns
 // 0 and a store past it is dropped by the hardware, so tile edges need no
@@ -128,6 +156,17 @@ template <> struct BufIO<uint16_t> {
     __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint32_t v) {
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(i * 2u), 0,
                                               LRS_STORE_POLICY);
+    }
+};
+template <> struct BufIO<uint64_t> {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    __device__ static inline uint64_t load(__amdgpu_buffer_rsrc_t r, uint32_t i) {
+        const v2u w = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(i * 8u), 0, LRS_LOAD_POLICY);
+        return (static_cast<uint64_t>(w.y) << 32) | w.x;
+    }
+    __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t i, uint64_t v) {
+        const v2u w = {static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(i * 8u), 0, LRS_STORE_POLICY);
     }
 };
 template <> struct BufIO<int64_t> {
@@ -231,8 +270,8 @@ struct SweepArgs {
     uint32_t hist_row_stride;
     uint32_t shift;          // lowest bit of this pass's digit
     uint32_t digit_mask;     // (1 << width) - 1
-    uint32_t flip;           // key transform masks (see KeyTraits)
-    uint32_t flip_neg;
+    uint64_t flip;           // key transform masks (see KeyTraits)
+    uint64_t flip_neg;
     uint32_t spin_limit;     // polls of an unpublished look-back word before the tile counts
                              // its prefix from the keys; 0: always count from the keys
     // Reduce-then-scan (partition) mode: workgroup g sorts tiles
@@ -317,13 +356,15 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     static_assert(BLOCK % kWave == 0 && BLOCK >= static_cast<int>(R), "one thread per digit");
     static_assert(MATCH != kMatchLds || WAVES * R * 8 <= TILE * 4, "match masks must fit in the tile buffer");
     using Stored = typename KeyTraits<KK>::Stored;
+    using Word = typename KeyTraits<KK>::Word;
     using St = Status<W>;
 
     // s_buf holds the tile in digit order (keys, then payload); during the
     // ranking its front holds the per-wave digit masks of the LDS matching.
     // Between writing the keys and the payload out of the same slots, each
     // thread keeps its slots' digits in registers, four to a word.
-    __shared__ uint32_t s_buf[TILE];
+    __shared__ Word s_buf[TILE];
+    uint32_t *const s_pay = reinterpret_cast<uint32_t *>(s_buf);  // the payload's view of the slots
     __shared__ uint32_t s_cnt[WAVES][R];      // per-wave digit counts, then per-wave bases
     __shared__ uint32_t s_goff[R];            // output index of digit run start minus local start
     __shared__ uint32_t s_tmp[WAVES];
@@ -374,7 +415,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     // 1. Keys.  Elements past the end of the row read as 0 and take the
     // largest digit: last in input order, they rank after every real key of
     // that digit and are never written.
-    uint32_t key[ITEMS];
+    Word key[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, wbase + j * kWave + lane);
 
@@ -388,7 +429,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t p = wbase + j * kWave + lane;
-            const uint32_t dig = (KeyTraits<KK>::key(key[j], a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
+            const uint32_t dig = digit_of<KK>(key[j], a.flip, a.flip_neg, a.shift, a.digit_mask);
             const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
             uint32_t below, size;
             if constexpr (MATCH == kMatchBallot) {
@@ -523,7 +564,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             __syncthreads();
             const Stored *row_keys = static_cast<const Stored *>(a.keys_in) + row_base;
             for (uint32_t i = tid; i < tile_start; i += BLOCK) {
-                const uint32_t d = (KeyTraits<KK>::key(row_keys[i], a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
+                const uint32_t d = digit_of<KK>(row_keys[i], a.flip, a.flip_neg, a.shift, a.digit_mask);
                 atomicAdd(&s_goff[d], 1u);
             }
             __syncthreads();
@@ -551,8 +592,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const uint32_t k = i * BLOCK + tid;
-        const uint32_t v = s_buf[k];
-        const uint32_t d = (KeyTraits<KK>::key(v, a.flip, a.flip_neg) >> a.shift) & a.digit_mask;
+        const Word v = s_buf[k];
+        const uint32_t d = digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
         if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
         const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
         if constexpr (kWide) {
@@ -569,7 +610,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             uint32_t v;
             if constexpr (PK == kPayIdxFirst) v = tile_start + wbase + j * kWave + lane;
             else v = val[j];
-            s_buf[rank[j]] = v;
+            s_pay[rank[j]] = v;
         }
         __syncthreads();
         using OutT = typename std::conditional<PK == kPayIdxLast, int64_t, uint32_t>::type;
@@ -581,9 +622,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
             const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
             if constexpr (kWide) {
-                if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_buf[k]);
+                if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_pay[k]);
             } else {
-                BufIO<OutT>::store(vout_rsrc, dst, s_buf[k]);
+                BufIO<OutT>::store(vout_rsrc, dst, s_pay[k]);
             }
         }
     }
@@ -606,8 +647,8 @@ struct ResidentArgs {
     uint32_t row_len;        // elements per row, at most BLOCK * ITEMS
     uint32_t begin_bit;
     uint32_t end_bit;
-    uint32_t flip;           // key transform masks (see KeyTraits)
-    uint32_t flip_neg;
+    uint64_t flip;           // key transform masks (see KeyTraits)
+    uint64_t flip_neg;
 };
 
 // Payload of the resident sort.
@@ -749,12 +790,12 @@ struct HistArgs {
     uint32_t passes;
     uint32_t begin_bit;
     uint32_t end_bit;
-    uint32_t flip;           // key transform masks (see KeyTraits)
-    uint32_t flip_neg;
+    uint64_t flip;           // key transform masks (see KeyTraits)
+    uint64_t flip_neg;
     uint32_t atomic;         // 1: several workgroups per row accumulate; 0: one writes it
 };
 
-constexpr int kHistMaxCounters = 1024;  // passes * R for every legal (window, b)
+constexpr int kHistMaxCounters = 2048;  // passes * R for every legal (window, b, key width)
 constexpr int kHistCopies = LRS_HIST_COPIES;
 #ifndef LRS_HIST_BLOCK
 #define LRS_HIST_BLOCK 1024
@@ -776,34 +817,42 @@ template <int B, int KK>
 __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t R = 1u << B;
     using Stored = typename KeyTraits<KK>::Stored;
+    using Word = typename KeyTraits<KK>::Word;
     constexpr uint32_t kPerVec = 16u / sizeof(Stored);
     constexpr int kMaxPasses = (8 * static_cast<int>(sizeof(Stored)) + B - 1) / B;
-    constexpr uint32_t kPassWords = R * kHistCopies;
     static_assert(kMaxPasses * R <= kHistMaxCounters, "counters must fit");
+    // half the copies when the counters would not fit in 128 KB (8-bit digits of 64-bit keys)
+    constexpr int kCopies = (kMaxPasses * R * kHistCopies * 4 <= 131072) ? kHistCopies : kHistCopies / 2;
+    constexpr uint32_t kPassWords = R * kCopies;
     constexpr int kUnroll = 4;
-    __shared__ uint32_t s_h[kMaxPasses * R * kHistCopies];  // 128 KB for 8-bit digits of u32 keys
+    __shared__ uint32_t s_h[kMaxPasses * R * kCopies];  // 128 KB for 8-bit digits of u32 keys
 
     const uint32_t row = blockIdx.x / a.chunks_per_row;
     const uint32_t chunk = blockIdx.x - row * a.chunks_per_row;
     const uint32_t total = a.passes * R;
-    for (uint32_t i = threadIdx.x; i < total * kHistCopies; i += kHistBlock) s_h[i] = 0u;
+    for (uint32_t i = threadIdx.x; i < total * kCopies; i += kHistBlock) s_h[i] = 0u;
     __syncthreads();
 
-    uint32_t *mine = s_h + (threadIdx.x % kHistCopies);
-    auto count_key = [&](uint32_t v) {
-        const uint32_t k = KeyTraits<KK>::key(v, a.flip, a.flip_neg);
+    uint32_t *mine = s_h + (threadIdx.x % kCopies);
+    auto count_key = [&](Word v) {
+        const Word k = KeyTraits<KK>::key(v, a.flip, a.flip_neg);
 #pragma unroll
         for (int p = 0; p < kMaxPasses; ++p) {
             if (p < static_cast<int>(a.passes)) {
                 const uint32_t shift = a.begin_bit + static_cast<uint32_t>(p) * B;
                 const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
-                const uint32_t d = __builtin_amdgcn_ubfe(k, shift, width);
-                atomicAdd(mine + p * kPassWords + d * kHistCopies, 1u);
+                uint32_t d;
+                if constexpr (sizeof(Word) == 8) d = static_cast<uint32_t>(k >> shift) & ((1u << width) - 1u);
+                else d = __builtin_amdgcn_ubfe(k, shift, width);
+                atomicAdd(mine + p * kPassWords + d * kCopies, 1u);
             }
         }
     };
     auto count_vec = [&](const uint4 &w) {
-        if constexpr (sizeof(Stored) == 4) {
+        if constexpr (sizeof(Stored) == 8) {
+            count_key((static_cast<uint64_t>(w.y) << 32) | w.x);
+            count_key((static_cast<uint64_t>(w.w) << 32) | w.z);
+        } else if constexpr (sizeof(Stored) == 4) {
             count_key(w.x); count_key(w.y); count_key(w.z); count_key(w.w);
         } else {
             count_key(w.x & 0xFFFFu); count_key(w.x >> 16);
@@ -840,9 +889,9 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
         for (int u = 0; u < kUnroll; ++u) count_vec(w[u]);
     }
     for (; q < q_end; q += step) count_vec(v4[q]);
-    if (chunk == 0 && threadIdx.x < head) count_key(static_cast<uint32_t>(base[threadIdx.x]));
+    if (chunk == 0 && threadIdx.x < head) count_key(static_cast<Word>(base[threadIdx.x]));
     if (chunk == a.chunks_per_row - 1 && body_end + threadIdx.x < a.row_len)
-        count_key(static_cast<uint32_t>(base[body_end + threadIdx.x]));
+        count_key(static_cast<Word>(base[body_end + threadIdx.x]));
     __syncthreads();
 
     uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
@@ -851,8 +900,8 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
         uint32_t c = 0;
         // copies taken in a rotated order so neighbouring threads read different banks
 #pragma unroll
-        for (int k = 0; k < kHistCopies; ++k)
-            c += s_h[p * kPassWords + d * kHistCopies + ((k + i) % kHistCopies)];
+        for (int k = 0; k < kCopies; ++k)
+            c += s_h[p * kPassWords + d * kCopies + ((k + i) % kCopies)];
         if (a.atomic) {
             if (c) atomicAdd(out + i, c);
         } else {
@@ -871,7 +920,7 @@ struct PartArgs {
     uint32_t partitions;
     uint32_t shift;
     uint32_t digit_mask;
-    uint32_t flip, flip_neg;
+    uint64_t flip, flip_neg;
 };
 
 // Upsweep: the pass digit's count over each partition (one workgroup per

@@ -77,6 +77,10 @@ def _load():
     lib.oracle_key32.restype = c_int
     lib.oracle_radix_sort_typed.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int]
     lib.oracle_radix_sort_typed.restype = c_int
+    lib.oracle_key64.argtypes = [u64, c_int, c_int, P]
+    lib.oracle_key64.restype = c_int
+    lib.oracle_radix_sort_typed64.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int]
+    lib.oracle_radix_sort_typed64.restype = c_int
     _lib = lib
     return lib
 
@@ -174,7 +178,15 @@ def stable_position(keys: np.ndarray, begin_bit: int, end_bit: int, i: int) -> i
 
 # ------------------------------------------------------ typed 32-bit keys
 
-KEY_TYPES = {"u32": 0, "i32": 1, "f32": 2}
+KEY_TYPES = {"u32": 0, "i32": 1, "f32": 2, "u64": 3, "i64": 4, "f64": 5}
+
+
+def key64(bits: int, key_type: str, descending: bool = False) -> int:
+    """Order-preserving u64 image of one 64-bit pattern of the given type."""
+    out = np.zeros(1, dtype=np.uint64)
+    _check(_load().oracle_key64(int(bits) & 0xFFFFFFFFFFFFFFFF, KEY_TYPES[key_type], int(descending), _ptr(out)),
+           "key64")
+    return int(out[0])
 
 
 def key32(bits: int, key_type: str, descending: bool = False) -> int:
@@ -187,8 +199,18 @@ def key32(bits: int, key_type: str, descending: bool = False) -> int:
 
 def radix_sort_typed(keys, vals=None, key_type: str = "u32", descending: bool = False,
                      begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8):
-    """Stable sort of 32-bit keys (bit patterns of u32, i32 or f32) by their image's
-    bit window; returns (key patterns, vals-or-None) in sorted order."""
+    """Stable sort of 32- or 64-bit keys (bit patterns of u32/i32/f32 or u64/i64/f64) by
+    their image's bit window; returns (key patterns, vals-or-None) in sorted order."""
+    if key_type.endswith("64"):
+        k = np.ascontiguousarray(np.asarray(keys).view(np.uint64))
+        v = None if vals is None else _u32(vals)
+        if v is not None and v.size != k.size:
+            raise ValueError("keys and vals differ in length")
+        ko = np.empty_like(k)
+        vo = None if v is None else np.empty_like(v)
+        _check(_load().oracle_radix_sort_typed64(_ptr(k), _ptr(v), _ptr(ko), _ptr(vo), k.size, KEY_TYPES[key_type],
+                                                 int(descending), begin_bit, end_bit, digit_bits), "radix_sort_typed64")
+        return ko, vo
     k = np.ascontiguousarray(np.asarray(keys).view(np.uint32))
     v = None if vals is None else _u32(vals)
     if v is not None and v.size != k.size:

@@ -27,8 +27,9 @@
  *    the descending flag into that conversion).  Reading: negative patterns are
  *    bit-complemented, non-negative patterns get the sign bit set; descending
  *    is the complement of the ascending key, so ties keep input order.
- *  - The same kind of map for 32-bit signed integers and binary32 floats, and
- *    the stable sort of such keys (with an optional payload) by their image.
+ *  - The same kind of map for 32- and 64-bit signed integers and binary32 /
+ *    binary64 floats, and the stable sort of such keys (with an optional
+ *    payload) by their image.
  *
  * Every result here is unique (a stable sort of a fixed sequence has exactly one
  * output), so the GPU path is compared against it element for element.
@@ -309,6 +310,81 @@ int oracle_radix_sort_typed(const uint32_t *keys_in, const uint32_t *vals_in, ui
     }
 done:
     free(image); free(index); free(image_sorted); free(index_sorted);
+    return rc;
+}
+
+/*
+ * The same maps for 64-bit keys: key_type 3 = u64 (the value), 4 = i64 (add
+ * 2^63 modulo 2^64), 5 = f64 (IEEE binary64: complement negative patterns,
+ * set the sign bit of the others).  Descending: the complement.
+ */
+int oracle_key64(uint64_t bits, int key_type, int descending, uint64_t *out)
+{
+    const uint64_t top = 0x8000000000000000ull;
+    uint64_t asc;
+    if (key_type == 3) {
+        asc = bits;
+    } else if (key_type == 4) {
+        asc = bits + top;
+    } else if (key_type == 5) {
+        asc = (bits & top) ? ~bits : (bits | top);
+    } else {
+        return ORACLE_EINVAL;
+    }
+    *out = descending ? ~asc : asc;
+    return ORACLE_OK;
+}
+
+/*
+ * Stable LSD sort of n 64-bit keys (optional u32 payload) by the bit window
+ * [begin_bit, end_bit) of their image: one counting-sort pass per b-bit digit,
+ * low digit first, moving (image, input index); then the original key bits and
+ * payloads are gathered in the sorted index order.
+ */
+int oracle_radix_sort_typed64(const uint64_t *keys_in, const uint32_t *vals_in, uint64_t *keys_out,
+                              uint32_t *vals_out, uint64_t n, int key_type, int descending,
+                              int begin_bit, int end_bit, int digit_bits)
+{
+    if (!check_window(begin_bit, end_bit, 64, digit_bits) || n > 0xFFFFFFFFull) return ORACLE_EINVAL;
+    if (n == 0) return ORACLE_OK;
+    if (!keys_in || !keys_out || ((vals_in == NULL) != (vals_out == NULL))) return ORACLE_EINVAL;
+    uint32_t radix = 1u << digit_bits;
+    int passes = oracle_num_passes(begin_bit, end_bit, digit_bits);
+    uint64_t *img = (uint64_t *)malloc(sizeof(uint64_t) * n);
+    uint64_t *img2 = (uint64_t *)malloc(sizeof(uint64_t) * n);
+    uint32_t *idx = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    uint32_t *idx2 = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    uint32_t *digit = (uint32_t *)malloc(sizeof(uint32_t) * n);
+    uint64_t *dest = (uint64_t *)malloc(sizeof(uint64_t) * n);
+    uint64_t *count = (uint64_t *)malloc(sizeof(uint64_t) * radix);
+    uint64_t *offset = (uint64_t *)malloc(sizeof(uint64_t) * radix);
+    int rc = ORACLE_OK;
+    if (!img || !img2 || !idx || !idx2 || !digit || !dest || !count || !offset) { rc = ORACLE_ENOMEM; goto done; }
+    for (uint64_t i = 0; i < n; i++) {
+        rc = oracle_key64(keys_in[i], key_type, descending, &img[i]);
+        if (rc != ORACLE_OK) goto done;
+        idx[i] = (uint32_t)i;
+    }
+    for (int p = 0; p < passes; p++) {
+        int shift = begin_bit + p * digit_bits;
+        int width = (end_bit - shift < digit_bits) ? (end_bit - shift) : digit_bits;
+        uint64_t mask = (1ull << width) - 1ull;
+        for (uint64_t i = 0; i < n; i++) digit[i] = (uint32_t)((img[i] >> shift) & mask);
+        rc = oracle_counting_pass(digit, n, radix, count, offset, dest);
+        if (rc != ORACLE_OK) goto done;
+        for (uint64_t i = 0; i < n; i++) {
+            img2[dest[i]] = img[i];
+            idx2[dest[i]] = idx[i];
+        }
+        uint64_t *ti = img; img = img2; img2 = ti;
+        uint32_t *tx = idx; idx = idx2; idx2 = tx;
+    }
+    for (uint64_t i = 0; i < n; i++) {
+        keys_out[i] = keys_in[idx[i]];
+        if (vals_in) vals_out[i] = vals_in[idx[i]];
+    }
+done:
+    free(img); free(img2); free(idx); free(idx2); free(digit); free(dest); free(count); free(offset);
     return rc;
 }
 

@@ -116,3 +116,77 @@ def test_typed_rejects_unknown_key_type():
     st = lib.radix_sort_keys_typed(k.data_ptr(), o.data_ptr(), 16, 7, 0, 0, 32, 8, ws.data_ptr(), 1,
                                    torch.cuda.current_stream().cuda_stream)
     assert st == 7  # LRS_ERR_DTYPE
+
+
+# ------------------------------------------------------------- 64-bit keys
+
+SPECIAL_F64 = np.array([0xFFF8000000000000, 0xFFF0000000000000, 0xFFEFFFFFFFFFFFFF, 0xBFF0000000000000,
+                        0x8000000000000001, 0x8000000000000000, 0x0000000000000000, 0x0000000000000001,
+                        0x3FF0000000000000, 0x7FEFFFFFFFFFFFFF, 0x7FF0000000000000, 0x7FF8000000000000,
+                        0x7FF8000000000001, 0xFFFFFFFFFFFFFFFF], dtype=np.uint64)
+
+
+def make_keys64(key_type: str, n: int, seed: int) -> np.ndarray:
+    """Bit patterns (uint64) of n keys of the type, with ties and special values."""
+    if key_type == "f64":
+        x = workloads.normal_f64(seed, n)
+        x[::5] = np.round(x[::5] * 4) / 4
+        bits = x.view(np.uint64).copy()
+        bits[3::97] = SPECIAL_F64[np.arange(bits[3::97].size) % SPECIAL_F64.size]
+        return bits
+    hi = workloads.random_u32(seed, n).astype(np.uint64)
+    lo = workloads.random_u32(seed + 7, n).astype(np.uint64)
+    bits = (hi << np.uint64(32)) | lo
+    bits[1::3] = bits[1::3] % np.uint64(64)  # ties, small positives
+    if key_type == "i64":
+        small_negative = -(bits[2::11] % np.uint64(64)).astype(np.int64) - 1
+        bits[2::11] = small_negative.view(np.uint64)
+    return bits
+
+
+def check64(bits, key_type, descending, b, begin=0, end=64):
+    kt = torch.from_numpy(bits.view(np.int64).copy()).cuda()
+    if key_type == "f64":
+        kt = kt.view(torch.float64)
+    vals = np.arange(bits.size, dtype=np.uint32) * np.uint32(2654435761)
+    vt = torch.from_numpy(vals.view(np.int32).copy()).cuda()
+    for with_vals in (False, True):
+        if with_vals:
+            ko, vo = lrs.radix_sort_pairs_typed(kt, vt, descending, key_type, begin, end, b)
+        else:
+            ko, vo = lrs.radix_sort_keys_typed(kt, descending, key_type, begin, end, b), None
+        torch.cuda.synchronize()
+        gk = ko.view(torch.int64).cpu().numpy().view(np.uint64)
+        ek, ev = oracle.radix_sort_typed(bits, vals if with_vals else None, key_type, descending, begin, end, b)
+        bad = np.flatnonzero(gk != ek)
+        assert bad.size == 0, f"{key_type} desc={descending} b={b} keys differ at {bad[:5]} (of {bad.size})"
+        if with_vals:
+            gv = vo.cpu().numpy().view(np.uint32)
+            bad = np.flatnonzero(gv != ev)
+            assert bad.size == 0, f"{key_type} desc={descending} b={b} values differ at {bad[:5]} (of {bad.size})"
+
+
+@pytest.mark.parametrize("key_type", ["i64", "f64", "u64"])
+@pytest.mark.parametrize("n", [1, 1000, 8193, 300_001, 1_200_007, 2_500_003])
+def test_typed64_sizes(key_type, n):
+    # 2048-, 4096- and 8192-key tile shapes of 64-bit keys
+    bits = make_keys64(key_type, n, 6100 + n % 1000)
+    for descending in (False, True):
+        log(f"{key_type} n={n} desc={descending}")
+        check64(bits, key_type, descending, 8)
+
+
+@pytest.mark.parametrize("key_type", ["i64", "f64"])
+@pytest.mark.parametrize("b", [2, 4])
+def test_typed64_digit_widths(key_type, b):
+    bits = make_keys64(key_type, 40_003, 6200 + b)
+    for descending in (False, True):
+        log(f"{key_type} b={b} desc={descending}")
+        check64(bits, key_type, descending, b)
+
+
+def test_typed64_one_bit_digits_and_windows():
+    bits = make_keys64("i64", 5003, 6300)
+    check64(bits, "i64", False, 1)            # 64 one-bit passes
+    check64(bits, "i64", True, 4, 16, 48)     # a middle window of the image
+    check64(make_keys64("u64", 70_001, 6301), "u64", False, 8, 0, 40)

@@ -1,5 +1,5 @@
-"""Pins of the oracle's typed 32-bit sort (signed integers, binary32 floats,
-descending order) against numpy's stable sort, the plain definition of a
+"""Pins of the oracle's typed 32- and 64-bit sorts (signed integers, binary32
+and binary64 floats, descending order) against numpy's stable sort, the plain definition of a
 descending stable order, the real-number order of floats, and a hand-ordered
 list of special float patterns (Day 35 "Pitfalls": floats and signed integers
 sort as unsigned integers after an order-preserving map)."""
@@ -113,4 +113,81 @@ def test_digit_widths_agree(key_type):
     ref = oracle.radix_sort_typed(x, vals, key_type, True, 0, 32, 8)
     for b in (1, 2, 4):
         got = oracle.radix_sort_typed(x, vals, key_type, True, 0, 32, b)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+# ------------------------------------------------------------- 64-bit keys
+
+SPECIAL_F64_IN_ORDER = [
+    0xFFF8000000000000,  # -NaN
+    0xFFF0000000000000,  # -inf
+    0xFFEFFFFFFFFFFFFF,  # -max
+    0xBFF0000000000000,  # -1
+    0x8000000000000001,  # -smallest subnormal
+    0x8000000000000000,  # -0
+    0x0000000000000000,  # +0
+    0x0000000000000001,  # +smallest subnormal
+    0x3FF0000000000000,  # +1
+    0x7FEFFFFFFFFFFFFF,  # +max
+    0x7FF0000000000000,  # +inf
+    0x7FF8000000000000,  # +NaN
+]
+
+
+def _i64(n, seed):
+    hi = workloads.random_u32(seed, n).astype(np.uint64)
+    lo = workloads.random_u32(seed + 1, n).astype(np.uint64)
+    return ((hi << np.uint64(32)) | lo).view(np.int64).copy()
+
+
+@pytest.mark.parametrize("n", [1, 17, 5000])
+def test_i64_against_numpy_and_definition(n):
+    x = _i64(n, 1100 + n)
+    if n >= 4:
+        x[:4] = [np.iinfo(np.int64).min, np.iinfo(np.int64).max, 0, -1]
+    x[n // 2:] = x[n // 2:] % 97 - 48
+    asc = _perm64(x, "i64", False)
+    assert np.array_equal(asc, np.argsort(x, kind="stable"))
+    assert np.array_equal(_perm64(x, "i64", True), _desc_stable([int(v) for v in x]))
+
+
+def _perm64(keys, key_type, descending, b=8, begin=0, end=64):
+    n = len(keys)
+    _, idx = oracle.radix_sort_typed(keys, np.arange(n, dtype=np.uint32), key_type, descending, begin, end, b)
+    return idx.astype(np.int64)
+
+
+@pytest.mark.parametrize("n", [3, 5000])
+def test_f64_against_numpy_and_definition(n):
+    x = workloads.normal_f64(1200 + n, n)
+    x[::7] = np.round(x[::7])
+    x[x == 0] = 0.0
+    assert np.array_equal(_perm64(x, "f64", False), np.argsort(x, kind="stable"))
+    assert np.array_equal(_perm64(x, "f64", True), _desc_stable([float(v) for v in x]))
+
+
+def test_f64_special_values_order():
+    order = np.array(SPECIAL_F64_IN_ORDER, dtype=np.uint64)
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        shuffled = order[rng.permutation(order.size)]
+        assert np.array_equal(oracle.radix_sort_typed(shuffled, None, "f64", False, 0, 64)[0], order)
+        assert np.array_equal(oracle.radix_sort_typed(shuffled, None, "f64", True, 0, 64)[0], order[::-1])
+
+
+def test_u64_descending_definition_and_window():
+    x = _i64(3000, 1300).view(np.uint64) % np.uint64(10 ** 12)
+    assert np.array_equal(_perm64(x, "u64", True), _desc_stable([int(v) for v in x]))
+    # the top 16 bits of the i64 image order like the arithmetic shift of the value by 48
+    y = _i64(3000, 1310)
+    assert np.array_equal(_perm64(y, "i64", False, 4, 48, 64), np.argsort(y >> 48, kind="stable"))
+
+
+@pytest.mark.parametrize("key_type", ["i64", "f64"])
+def test_digit_widths_agree_64(key_type):
+    x = _i64(2000, 1400) if key_type == "i64" else workloads.normal_f64(1401, 2000)
+    vals = np.arange(x.size, dtype=np.uint32)
+    ref = oracle.radix_sort_typed(x, vals, key_type, False, 0, 64, 8)
+    for b in (2, 4):
+        got = oracle.radix_sort_typed(x, vals, key_type, False, 0, 64, b)
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])

@@ -116,6 +116,8 @@ WORKLOADS = {
                                 descending=True, digit_bits=(8,)),
     "i32_keys_2p28_asc": dict(index=6, kind="typed_keys", n=1 << 28, key_type="i32",
                               descending=False, digit_bits=(8,)),
+    "f64_pairs_2p27_asc": dict(index=7, kind="typed_pairs", n=1 << 27, key_type="f64",
+                               descending=False, digit_bits=(8,)),
 }
 
 
@@ -158,6 +160,11 @@ def keys_f32_normal(n: int = 1 << 28) -> np.ndarray:
     """Bit patterns (uint32) of N(0,1) draws (Box-Muller in fp64) rounded to
     binary32; the typed-key workload."""
     return normal_f64(seed_of(5), n).astype(np.float32).view(np.uint32)
+
+
+def keys_f64_normal(n: int = 1 << 27) -> np.ndarray:
+    """Bit patterns (uint64) of N(0,1) draws (Box-Muller in fp64)."""
+    return normal_f64(seed_of(7), n).view(np.uint64)
 
 
 def keys_i32_uniform(n: int = 1 << 28) -> np.ndarray:
