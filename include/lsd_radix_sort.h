@@ -104,6 +104,18 @@ int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t 
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * As segmented_row_sort, but each element carries a caller-supplied u32
+ * payload instead of the column index: pay_out[r][j] is the payload of the
+ * element that lands at vals_out[r][j] (the payload rides along with every
+ * move of its key).  pay_in / pay_out are row-major rows x n u32, 4-byte
+ * aligned, and must not overlap each other, the values or the workspace.  The
+ * workspace is segmented_row_sort_workspace_size(rows, n, digit_bits).
+ */
+int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out,
+                             uint32_t *pay_out, int64_t rows, int64_t n, int dtype, int descending,
+                             int digit_bits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Stable LSD sort of n 32- or 64-bit keys of type key_type, ascending or
  * descending, with or without a u32 payload.  The sort orders the key's
  * order-preserving unsigned image (100 Days of GPU, Day 35, "Pitfalls": a

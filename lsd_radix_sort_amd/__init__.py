@@ -76,6 +76,8 @@ def load_library():
     lib.segmented_row_sort_workspace_size.restype = szt
     lib.segmented_row_sort.argtypes = [P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P]
     lib.segmented_row_sort.restype = c_int
+    lib.segmented_row_sort_pairs.argtypes = [P, P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P]
+    lib.segmented_row_sort_pairs.restype = c_int
     lib.radix_sort_digit_histograms.argtypes = [P, u64, c_int, c_int, c_int, P, P]
     lib.radix_sort_digit_histograms.restype = c_int
     lib.radix_sort_copy_probe.argtypes = [P, P, szt, P]
@@ -281,6 +283,38 @@ def segmented_row_sort(x: torch.Tensor, descending: bool = False, digit_bits: in
                                   int(descending), digit_bits, _ptr(workspace), workspace.numel(),
                                   _stream(x)), "segmented_row_sort")
     return values_out, indices_out
+
+
+def segmented_row_sort_pairs(x: torch.Tensor, payload: torch.Tensor, descending: bool = False,
+                             digit_bits: int = 8, values_out: torch.Tensor | None = None,
+                             payload_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Sort every row of a 2-D fp16/bf16 GPU tensor carrying a same-shape 32-bit payload;
+    returns (values, payload)."""
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if x.dtype == torch.float16:
+        dtype = LRS_DTYPE_FP16
+    elif x.dtype == torch.bfloat16:
+        dtype = LRS_DTYPE_BF16
+    else:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    if (not isinstance(payload, torch.Tensor) or not payload.is_cuda or payload.shape != x.shape
+            or payload.element_size() != 4 or not payload.is_contiguous()):
+        raise ValueError("payload must be a contiguous 32-bit GPU tensor of x's shape")
+    rows, n = x.shape
+    if values_out is None:
+        values_out = torch.empty_like(x)
+    if payload_out is None:
+        payload_out = torch.empty_like(payload)
+    if workspace is None:
+        workspace = _workspace(lib.segmented_row_sort_workspace_size(rows, n, digit_bits), x.device)
+    _check(lib.segmented_row_sort_pairs(_ptr(x), _ptr(payload), _ptr(values_out), _ptr(payload_out), rows, n,
+                                        dtype, int(descending), digit_bits, _ptr(workspace), workspace.numel(),
+                                        _stream(x)), "segmented_row_sort_pairs")
+    return values_out, payload_out
 
 
 def radix_sort_digit_histograms(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,

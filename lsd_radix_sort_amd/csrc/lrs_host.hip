@@ -774,6 +774,72 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
     return LRS_OK;
 }
 
+int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out,
+                             uint32_t *pay_out, int64_t rows, int64_t n, int dtype, int descending,
+                             int digit_bits, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
+    if (dtype != LRS_DTYPE_FP16 && dtype != LRS_DTYPE_BF16) return LRS_ERR_DTYPE;
+    if (rows < 0 || n < 0 || static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
+        (rows > 0 && static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40)))
+        return LRS_ERR_SIZE;
+    if (rows == 0 || n == 0) return LRS_OK;
+    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2);
+    if (!vals_in || !vals_out || !pay_in || !pay_out || (p.total && !workspace)) return LRS_ERR_NULL_POINTER;
+    if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(pay_in, 4) || misaligned(pay_out, 4) ||
+        misaligned(workspace, 256))
+        return LRS_ERR_ALIGNMENT;
+    if (p.num_tiles > 0x7FFFFFFFull || p.rows * p.hist_chunks_per_row > 0x7FFFFFFFull) return LRS_ERR_SIZE;
+    if (workspace_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
+    const uint64_t cnt = static_cast<uint64_t>(rows) * n;
+    if (overlaps(vals_out, 2 * cnt, vals_in, 2 * cnt) || overlaps(vals_out, 2 * cnt, pay_in, 4 * cnt) ||
+        overlaps(pay_out, 4 * cnt, vals_in, 2 * cnt) || overlaps(pay_out, 4 * cnt, pay_in, 4 * cnt) ||
+        overlaps(pay_out, 4 * cnt, vals_out, 2 * cnt) || overlaps(vals_out, 2 * cnt, workspace, p.total) ||
+        overlaps(pay_out, 4 * cnt, workspace, p.total))
+        return LRS_ERR_ALIASING;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t flip = descending ? 0xFFFFu : 0u;
+    if (p.resident) {
+        if (rows > 0x7FFFFFFF) return LRS_ERR_SIZE;
+        ResidentArgs r{};
+        r.keys_in = vals_in;
+        r.keys_out = vals_out;
+        r.vals_in = pay_in;
+        r.vals_out = pay_out;
+        r.row_len = static_cast<uint32_t>(n);
+        r.begin_bit = 0;
+        r.end_bit = 16;
+        r.flip = flip;
+        const hipError_t e = launch_resident<kKeyF16, kResU32>(digit_bits, r, rows, n, s);
+        return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    }
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
+    uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
+    uint32_t *alt_p = reinterpret_cast<uint32_t *>(ws + p.off_idx[0]);
+    const uint16_t *src_k = vals_in;
+    const uint32_t *src_p = pay_in;
+    for (int pass = 0; pass < p.passes; ++pass) {
+        SweepArgs a = pass_args(p, ws, pass);
+        a.flip = flip;
+        uint16_t *dk = pass_dst(pass, p.passes, vals_out, alt_k);
+        uint32_t *dp = pass_dst(pass, p.passes, pay_out, alt_p);
+        a.keys_in = src_k;
+        a.keys_out = dk;
+        a.vals_in = src_p;
+        a.vals_out = dp;
+        TimedLaunch t(2, s);
+        const hipError_t e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+        src_k = dk;
+        src_p = dp;
+    }
+    return LRS_OK;
+}
+
 int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit,
                                 int digit_bits, uint32_t *hist_out, void *stream) {
     if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;

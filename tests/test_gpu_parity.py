@@ -303,6 +303,28 @@ def test_rows_ragged_shapes(rows, n, b):
             assert_same(gi.ravel(), ei.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype} idx")
 
 
+@pytest.mark.parametrize("rows,n", [(3, 7), (5, 4095), (3, 8192), (3, 8193), (7, 12345), (2, 200_000),
+                                     (64, 65536)])
+@pytest.mark.parametrize("b", [4, 8])
+def test_rows_with_caller_payload(rows, n, b):
+    # the payload must land where the oracle's column index says its element went
+    bits = workloads.fp16_normal_bits(rows * 977 + n, rows * n).reshape(rows, n)
+    bits[:, ::13] = np.uint16(0x8000)
+    payload = (workloads.random_u32(rows + 3 * n, rows * n)).reshape(rows, n)
+    for desc in (False, True):
+        ev, ei = oracle.segmented_row_sort(bits, desc, b)
+        expected_pay = np.take_along_axis(payload, ei, axis=1)
+        for dtype in ("fp16", "bf16"):
+            t = to_gpu(bits).view(torch.float16 if dtype == "fp16" else torch.bfloat16).reshape(rows, n)
+            pt = to_gpu(payload.ravel()).reshape(rows, n)
+            vo, po = lrs.segmented_row_sort_pairs(t, pt, desc, b)
+            torch.cuda.synchronize()
+            gv = vo.view(torch.int16).cpu().numpy().view(np.uint16)
+            gp = po.cpu().numpy().view(np.uint32)
+            assert_same(gv.ravel(), ev.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype} values")
+            assert_same(gp.ravel(), expected_pay.ravel(), f"rows={rows} n={n} b={b} desc={desc} {dtype} payload")
+
+
 # ------------------------------------------------ bounded look-back waits
 
 @pytest.fixture
