@@ -402,238 +402,238 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     }
     if (t_first >= a.num_tiles) return;  // not with zeroed counters and grid == num_tiles
     for (uint32_t t = t_first; t < t_end; ++t) {
-    const uint32_t row = t / a.tiles_per_row;
-    const uint32_t tile_in_row = t - row * a.tiles_per_row;
-    const uint32_t tile_start = tile_in_row * TILE;
-    const uint32_t valid = min(TILE, a.row_len - tile_start);
-    const uint64_t row_base = static_cast<uint64_t>(row) * a.row_len;
+        const uint32_t row = t / a.tiles_per_row;
+        const uint32_t tile_in_row = t - row * a.tiles_per_row;
+        const uint32_t tile_start = tile_in_row * TILE;
+        const uint32_t valid = min(TILE, a.row_len - tile_start);
+        const uint64_t row_base = static_cast<uint64_t>(row) * a.row_len;
 
-    const Stored *kin = static_cast<const Stored *>(a.keys_in) + row_base + tile_start;
-    const uint32_t wbase = static_cast<uint32_t>(wave) * kWave * ITEMS;
-    const __amdgpu_buffer_rsrc_t kin_rsrc = make_rsrc(kin, valid * sizeof(Stored));
+        const Stored *kin = static_cast<const Stored *>(a.keys_in) + row_base + tile_start;
+        const uint32_t wbase = static_cast<uint32_t>(wave) * kWave * ITEMS;
+        const __amdgpu_buffer_rsrc_t kin_rsrc = make_rsrc(kin, valid * sizeof(Stored));
 
-    // 1. Keys.  Elements past the end of the row read as 0 and take the
-    // largest digit: last in input order, they rank after every real key of
-    // that digit and are never written.
-    Word key[ITEMS];
+        // 1. Keys.  Elements past the end of the row read as 0 and take the
+        // largest digit: last in input order, they rank after every real key of
+        // that digit and are never written.
+        Word key[ITEMS];
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, wbase + j * kWave + lane);
+        for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, wbase + j * kWave + lane);
 
-    // 2. Stable rank inside the wave; the group's lowest lane advances the
-    // running count (and clears the mask).
-    const uint64_t lane_bit = 1ull << lane;
-    uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's digit
-    // Only a row's last tile has elements past the end, so full tiles take a
-    // copy of the loop without the bounds test.
-    auto rank_items = [&](auto partial) {
+        // 2. Stable rank inside the wave; the group's lowest lane advances the
+        // running count (and clears the mask).
+        const uint64_t lane_bit = 1ull << lane;
+        uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's digit
+        // Only a row's last tile has elements past the end, so full tiles take a
+        // copy of the loop without the bounds test.
+        auto rank_items = [&](auto partial) {
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t p = wbase + j * kWave + lane;
-            const uint32_t dig = digit_of<KK>(key[j], a.flip, a.flip_neg, a.shift, a.digit_mask);
-            const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
-            uint32_t below, size;
-            if constexpr (MATCH == kMatchBallot) {
-                group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
-            } else {
-                atomicOr(&s_match[wave][d], static_cast<unsigned long long>(lane_bit));
-                group_rank_from_members(s_match[wave][d], below, size);
-            }
-            const uint32_t before = s_cnt[wave][d];
-            rank[j] = (d << 16) | (before + below);
-            pin(rank[j]);
-            if (below == 0u) {
-                s_cnt[wave][d] = before + size;
-                if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
-            }
-        }
-    };
-    if (valid == TILE) rank_items(std::false_type{});
-    else rank_items(std::true_type{});
-    __syncthreads();
-
-    // 3. Digit d is owned by thread d.
-    uint32_t count = 0u;
-    if (tid < static_cast<int>(R)) {
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const uint32_t c = s_cnt[w][tid];
-            s_cnt[w][tid] = count;
-            count += c;
-        }
-    }
-    uint32_t real = count;  // padding is not part of the count of the last digit
-    if (tid == static_cast<int>(R) - 1) real -= TILE - valid;
-    W *status = static_cast<W *>(a.status) + static_cast<uint64_t>(t) * R;
-    if (!PART && tid < static_cast<int>(R))
-        publish(status + tid, static_cast<W>((tile_in_row == 0 ? St::kInclusive : St::kAggregate) |
-                                             static_cast<W>(real)));
-    const uint32_t local_start = block_exclusive_scan_n<BLOCK>(count, s_tmp, lane, wave);
-    uint32_t bucket_base = 0u;
-    if constexpr (!PART) {
-        const uint32_t hcount = (tid < static_cast<int>(R))
-            ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
-        bucket_base = block_exclusive_scan_n<BLOCK>(hcount, s_tmp, lane, wave);
-    }
-    if (tid < static_cast<int>(R)) {
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
-    }
-    __syncthreads();
-
-    // 4. Local reorder.
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const uint32_t d = rank[j] >> 16;
-        const uint32_t slot = s_cnt[wave][d] + (rank[j] & 0xFFFFu);
-        s_buf[slot] = key[j];
-        rank[j] = slot;
-    }
-
-    // Payload loads go out now, with the keys out of the registers, and are
-    // in flight while the look-back waits.
-    uint32_t val[ITEMS];
-    if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
-        const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
-        const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
-    }
-
-    // Look-back walk, one thread per digit.  Each round trip a lane reads its
-    // digit's words of the next kLookback predecessors (nearest first) and adds
-    // counts until an inclusive count or an unpublished word.  Lanes of a wave
-    // walk together; when none of a wave's lanes finds anything published, one
-    // lane polls a single word (with a short sleep) until the predecessor has
-    // published, instead of all of them re-reading memory.  The row's first
-    // tile publishes an inclusive count at once, so no walk leaves the row.
-    //
-    // Waiting is bounded: after spin_limit polls the wave gives up, and the
-    // workgroup counts the digit over the row's keys before this tile instead
-    // (the exact exclusive prefix, at the cost of reading them).  So no tile
-    // waits forever, whatever order the hardware starts workgroups in.
-    if constexpr (PART) {
-        if (tid < static_cast<int>(R)) {
-            s_goff[tid] = running - local_start;
-            running += real;
-        }
-    } else {
-        W excl = 0;
-        const bool from_keys = a.spin_limit == 0u && tile_in_row != 0u;
-        bool done = tile_in_row == 0 || from_keys || tid >= static_cast<int>(R);
-        bool gave_up = false;  // uniform in the wave
-        uint32_t polls = 0;
-        uint32_t back = 1;  // the next predecessor to consume is tile t - back
-        const W *row_status = static_cast<const W *>(a.status) + tid;
-        for (;;) {
-            const uint64_t walking = __builtin_amdgcn_ballot_w64(!done);
-            if (walking == 0 || gave_up) break;
-            W sv[kLookback];
-#pragma unroll
-            for (int i = 0; i < kLookback; ++i)
-                sv[i] = (!done && back + i <= tile_in_row)
-                    ? observe(row_status + static_cast<uint64_t>(t - back - i) * R) : W(0);
-            uint32_t used = 0;
-#pragma unroll
-            for (int i = 0; i < kLookback; ++i) {
-                const W flag = sv[i] & ~St::kMask;
-                if (done || used != static_cast<uint32_t>(i) || flag == 0) break;
-                excl += sv[i] & St::kMask;
-                used = i + 1;
-                done = flag == St::kInclusive;
-            }
-            back += used;
-            if (__builtin_amdgcn_ballot_w64(used != 0) == 0) {
-                const int leader = __builtin_ctzll(walking);
-                const W *word = row_status + static_cast<uint64_t>(t - back) * R;
-                for (;;) {
-                    if (++polls > a.spin_limit) {
-                        gave_up = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                    W pv = 0;
-                    if (lane == leader) pv = observe(word);
-                    if (__builtin_amdgcn_ballot_w64(lane == leader && (pv & ~St::kMask) != 0) != 0) break;
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t p = wbase + j * kWave + lane;
+                const uint32_t dig = digit_of<KK>(key[j], a.flip, a.flip_neg, a.shift, a.digit_mask);
+                const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
+                uint32_t below, size;
+                if constexpr (MATCH == kMatchBallot) {
+                    group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
+                } else {
+                    atomicOr(&s_match[wave][d], static_cast<unsigned long long>(lane_bit));
+                    group_rank_from_members(s_match[wave][d], below, size);
+                }
+                const uint32_t before = s_cnt[wave][d];
+                rank[j] = (d << 16) | (before + below);
+                pin(rank[j]);
+                if (below == 0u) {
+                    s_cnt[wave][d] = before + size;
+                    if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
                 }
             }
-        }
-        if (gave_up && lane == 0) s_gave_up = 1u;
+        };
+        if (valid == TILE) rank_items(std::false_type{});
+        else rank_items(std::true_type{});
         __syncthreads();
-        if (from_keys || s_gave_up != 0u) {
-            if (tid < static_cast<int>(R)) s_goff[tid] = 0u;
-            __syncthreads();
-            const Stored *row_keys = static_cast<const Stored *>(a.keys_in) + row_base;
-            for (uint32_t i = tid; i < tile_start; i += BLOCK) {
-                const uint32_t d = digit_of<KK>(row_keys[i], a.flip, a.flip_neg, a.shift, a.digit_mask);
-                atomicAdd(&s_goff[d], 1u);
+
+        // 3. Digit d is owned by thread d.
+        uint32_t count = 0u;
+        if (tid < static_cast<int>(R)) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const uint32_t c = s_cnt[w][tid];
+                s_cnt[w][tid] = count;
+                count += c;
             }
-            __syncthreads();
-            if (tid < static_cast<int>(R)) excl = s_goff[tid];
-            __syncthreads();
+        }
+        uint32_t real = count;  // padding is not part of the count of the last digit
+        if (tid == static_cast<int>(R) - 1) real -= TILE - valid;
+        W *status = static_cast<W *>(a.status) + static_cast<uint64_t>(t) * R;
+        if (!PART && tid < static_cast<int>(R))
+            publish(status + tid, static_cast<W>((tile_in_row == 0 ? St::kInclusive : St::kAggregate) |
+                                                 static_cast<W>(real)));
+        const uint32_t local_start = block_exclusive_scan_n<BLOCK>(count, s_tmp, lane, wave);
+        uint32_t bucket_base = 0u;
+        if constexpr (!PART) {
+            const uint32_t hcount = (tid < static_cast<int>(R))
+                ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
+            bucket_base = block_exclusive_scan_n<BLOCK>(hcount, s_tmp, lane, wave);
         }
         if (tid < static_cast<int>(R)) {
-            if (tile_in_row != 0)
-                publish(status + tid, static_cast<W>(St::kInclusive | (excl + real)));
-            s_goff[tid] = bucket_base + static_cast<uint32_t>(excl) - local_start;
-            if (a.status_next != nullptr)
-                static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
-        }
-    }
-    __syncthreads();
-
-    // 5. Keys out: slot k goes to s_goff[d] + k.  That is below row_len for
-    // every real element; the range check of the buffer store only keeps a
-    // logic error from becoming a stray store.
-    Stored *kout = static_cast<Stored *>(a.keys_out) + row_base;
-    uint32_t slot_digits[(ITEMS + 3) / 4];
 #pragma unroll
-    for (int i = 0; i < (ITEMS + 3) / 4; ++i) slot_digits[i] = 0u;
-    const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t k = i * BLOCK + tid;
-        const Word v = s_buf[k];
-        const uint32_t d = digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
-        if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
-        const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
-        if constexpr (kWide) {
-            if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
-        } else {
-            BufIO<Stored>::store(kout_rsrc, dst, v);
+            for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
         }
-    }
-
-    if constexpr (PK != kPayNone) {
         __syncthreads();
+
+        // 4. Local reorder.
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            uint32_t v;
-            if constexpr (PK == kPayIdxFirst) v = tile_start + wbase + j * kWave + lane;
-            else v = val[j];
-            s_pay[rank[j]] = v;
+            const uint32_t d = rank[j] >> 16;
+            const uint32_t slot = s_cnt[wave][d] + (rank[j] & 0xFFFFu);
+            s_buf[slot] = key[j];
+            rank[j] = slot;
+        }
+
+        // Payload loads go out now, with the keys out of the registers, and are
+        // in flight while the look-back waits.
+        uint32_t val[ITEMS];
+        if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
+            const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
+            const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
+        }
+
+        // Look-back walk, one thread per digit.  Each round trip a lane reads its
+        // digit's words of the next kLookback predecessors (nearest first) and adds
+        // counts until an inclusive count or an unpublished word.  Lanes of a wave
+        // walk together; when none of a wave's lanes finds anything published, one
+        // lane polls a single word (with a short sleep) until the predecessor has
+        // published, instead of all of them re-reading memory.  The row's first
+        // tile publishes an inclusive count at once, so no walk leaves the row.
+        //
+        // Waiting is bounded: after spin_limit polls the wave gives up, and the
+        // workgroup counts the digit over the row's keys before this tile instead
+        // (the exact exclusive prefix, at the cost of reading them).  So no tile
+        // waits forever, whatever order the hardware starts workgroups in.
+        if constexpr (PART) {
+            if (tid < static_cast<int>(R)) {
+                s_goff[tid] = running - local_start;
+                running += real;
+            }
+        } else {
+            W excl = 0;
+            const bool from_keys = a.spin_limit == 0u && tile_in_row != 0u;
+            bool done = tile_in_row == 0 || from_keys || tid >= static_cast<int>(R);
+            bool gave_up = false;  // uniform in the wave
+            uint32_t polls = 0;
+            uint32_t back = 1;  // the next predecessor to consume is tile t - back
+            const W *row_status = static_cast<const W *>(a.status) + tid;
+            for (;;) {
+                const uint64_t walking = __builtin_amdgcn_ballot_w64(!done);
+                if (walking == 0 || gave_up) break;
+                W sv[kLookback];
+#pragma unroll
+                for (int i = 0; i < kLookback; ++i)
+                    sv[i] = (!done && back + i <= tile_in_row)
+                        ? observe(row_status + static_cast<uint64_t>(t - back - i) * R) : W(0);
+                uint32_t used = 0;
+#pragma unroll
+                for (int i = 0; i < kLookback; ++i) {
+                    const W flag = sv[i] & ~St::kMask;
+                    if (done || used != static_cast<uint32_t>(i) || flag == 0) break;
+                    excl += sv[i] & St::kMask;
+                    used = i + 1;
+                    done = flag == St::kInclusive;
+                }
+                back += used;
+                if (__builtin_amdgcn_ballot_w64(used != 0) == 0) {
+                    const int leader = __builtin_ctzll(walking);
+                    const W *word = row_status + static_cast<uint64_t>(t - back) * R;
+                    for (;;) {
+                        if (++polls > a.spin_limit) {
+                            gave_up = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                        W pv = 0;
+                        if (lane == leader) pv = observe(word);
+                        if (__builtin_amdgcn_ballot_w64(lane == leader && (pv & ~St::kMask) != 0) != 0) break;
+                    }
+                }
+            }
+            if (gave_up && lane == 0) s_gave_up = 1u;
+            __syncthreads();
+            if (from_keys || s_gave_up != 0u) {
+                if (tid < static_cast<int>(R)) s_goff[tid] = 0u;
+                __syncthreads();
+                const Stored *row_keys = static_cast<const Stored *>(a.keys_in) + row_base;
+                for (uint32_t i = tid; i < tile_start; i += BLOCK) {
+                    const uint32_t d = digit_of<KK>(row_keys[i], a.flip, a.flip_neg, a.shift, a.digit_mask);
+                    atomicAdd(&s_goff[d], 1u);
+                }
+                __syncthreads();
+                if (tid < static_cast<int>(R)) excl = s_goff[tid];
+                __syncthreads();
+            }
+            if (tid < static_cast<int>(R)) {
+                if (tile_in_row != 0)
+                    publish(status + tid, static_cast<W>(St::kInclusive | (excl + real)));
+                s_goff[tid] = bucket_base + static_cast<uint32_t>(excl) - local_start;
+                if (a.status_next != nullptr)
+                    static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
+            }
         }
         __syncthreads();
-        using OutT = typename std::conditional<PK == kPayIdxLast, int64_t, uint32_t>::type;
-        OutT *vout = static_cast<OutT *>(a.vals_out) + row_base;
-        const __amdgpu_buffer_rsrc_t vout_rsrc = make_rsrc(vout, kWide ? 0u : a.row_len * sizeof(OutT));
+
+        // 5. Keys out: slot k goes to s_goff[d] + k.  That is below row_len for
+        // every real element; the range check of the buffer store only keeps a
+        // logic error from becoming a stray store.
+        Stored *kout = static_cast<Stored *>(a.keys_out) + row_base;
+        uint32_t slot_digits[(ITEMS + 3) / 4];
+#pragma unroll
+        for (int i = 0; i < (ITEMS + 3) / 4; ++i) slot_digits[i] = 0u;
+        const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
             const uint32_t k = i * BLOCK + tid;
-            const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
+            const Word v = s_buf[k];
+            const uint32_t d = digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
+            if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
             const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
             if constexpr (kWide) {
-                if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_pay[k]);
+                if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
             } else {
-                BufIO<OutT>::store(vout_rsrc, dst, s_pay[k]);
+                BufIO<Stored>::store(kout_rsrc, dst, v);
             }
         }
-    }
-    if constexpr (PART) {
-        // the next tile reuses the LDS: counters cleared, every read of this tile done
-        __syncthreads();
-        for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
-        __syncthreads();
-    }
+
+        if constexpr (PK != kPayNone) {
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                uint32_t v;
+                if constexpr (PK == kPayIdxFirst) v = tile_start + wbase + j * kWave + lane;
+                else v = val[j];
+                s_pay[rank[j]] = v;
+            }
+            __syncthreads();
+            using OutT = typename std::conditional<PK == kPayIdxLast, int64_t, uint32_t>::type;
+            OutT *vout = static_cast<OutT *>(a.vals_out) + row_base;
+            const __amdgpu_buffer_rsrc_t vout_rsrc = make_rsrc(vout, kWide ? 0u : a.row_len * sizeof(OutT));
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t k = i * BLOCK + tid;
+                const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
+                const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
+                if constexpr (kWide) {
+                    if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_pay[k]);
+                } else {
+                    BufIO<OutT>::store(vout_rsrc, dst, s_pay[k]);
+                }
+            }
+        }
+        if constexpr (PART) {
+            // the next tile reuses the LDS: counters cleared, every read of this tile done
+            __syncthreads();
+            for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
+            __syncthreads();
+        }
     }
 }
 

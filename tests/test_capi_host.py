@@ -104,6 +104,39 @@ def test_validation_before_launch():
     assert h(k_in, 100, 0, 32, 7, v_out, None) == 3
     assert h(k_in, 100, 0, 40, 8, v_out, None) == 2
     assert h(k_in, 100, 0, 32, 8, None, None) == 1
+    kt = lib.radix_sort_keys_typed
+    assert kt(k_in, k_out, 100, 9, 0, 0, 32, 8, ws, big, None) == 7      # unknown key type
+    assert kt(k_in, k_out, 100, 1, 0, 0, 33, 8, ws, big, None) == 2      # i32: at most 32 bits
+    assert kt(k_in, k_out, 100, 4, 0, 0, 65, 8, ws, big, None) == 2      # i64: at most 64 bits
+    assert kt(k_in, k_out, 100, 5, 1, 0, 64, 3, ws, big, None) == 3      # f64: digit width
+    assert kt(ctypes.c_void_p(0x10004), k_out, 100, 4, 0, 0, 64, 8, ws, big, None) == 9  # 8-byte keys
+    assert kt(k_in, k_out, 100, 4, 0, 0, 64, 8, None, big, None) == 1    # 64-bit keys need a workspace
+    assert kt(k_in, k_in, 100, 2, 0, 0, 32, 8, ws, big, None) == 5
+    pt = lib.radix_sort_pairs_typed
+    assert pt(k_in, None, k_out, v_out, 100, 2, 1, 0, 32, 8, ws, big, None) == 1
+    assert pt(k_in, v_in, k_out, v_out, 100, 6, 0, 0, 32, 8, ws, big, None) == 7
+    sg2 = lib.segmented_row_sort_pairs
+    assert sg2(k_in, None, k_out, v_out, 4, 100, 0, 0, 8, ws, big, None) == 1
+    assert sg2(k_in, v_in, k_out, v_in, 4, 100, 0, 0, 8, ws, big, None) == 5
+    assert sg2(k_in, v_in, k_out, v_out, 4, 100, 3, 0, 8, ws, big, None) == 7
+    assert sg2(None, None, None, None, 0, 100, 0, 0, 8, None, 0, None) == 0
+
+
+def test_typed_workspace_sizes_and_strategy_switch():
+    lib = lrs.load_library()
+    tws = lib.radix_sort_typed_workspace_size
+    # 32-bit types take the same workspace as the plain u32 sort
+    for kt in (0, 1, 2):
+        assert tws(1_000_000, kt, 0, 32, 8, 1) == lib.radix_sort_workspace_size(1_000_000, 0, 32, 8, 1)
+    assert tws(1000, 0, 0, 32, 8, 0) == 0                       # resident: no workspace
+    assert tws(1000, 3, 0, 64, 8, 0) > 0                        # 64-bit keys always need one
+    assert tws(1_000_000, 4, 0, 64, 8, 1) > tws(1_000_000, 1, 0, 32, 8, 1)
+    assert tws(100, 7, 0, 32, 8, 0) == 0 and tws(100, 4, 0, 65, 8, 0) == 0
+    assert lib.radix_sort_set_scan_strategy(2) == -1
+    old = lrs.radix_sort_set_scan_strategy("reduce-then-scan")
+    assert lrs.radix_sort_set_scan_strategy(old) == "reduce-then-scan"
+    with pytest.raises(ValueError):
+        lrs.radix_sort_set_scan_strategy("bogus")
 
 
 def test_python_binding_rejects_cpu_tensors():
