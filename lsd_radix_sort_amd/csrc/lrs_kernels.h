@@ -189,18 +189,26 @@ __device__ inline void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
 // leaves the lanes that differ in that bit, and the mismatch mask is the OR of
 // those over all bits.  v_bitop3 does XOR and OR in one instruction: with
 // operands (spread, acc, ballot) the table 0xDE is acc | (spread ^ ballot).
-// The ballot is taken from the spread itself (one compare); without the pin
-// the compiler derives it from d with a shift and a compare instead.
+// The ballots are taken from the spreads themselves (one compare each; the
+// pin stops the compiler from deriving them from d with a shift and a compare
+// instead), all before the accumulation, so each lands in its own scalar
+// register pair and no compare waits on the one before it.
 template <int B>
 __device__ inline uint64_t mismatch_mask(uint32_t d) {
+    uint32_t spread[B];
+    uint64_t bal[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+        spread[i] = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), i, 1));
+        pin(spread[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i) bal[i] = __builtin_amdgcn_ballot_w64(spread[i] != 0u);
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-        uint32_t spread = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), i, 1));
-        pin(spread);
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(spread != 0u);
-        lo = __builtin_amdgcn_bitop3_b32(spread, lo, static_cast<uint32_t>(bal), 0xDE);
-        hi = __builtin_amdgcn_bitop3_b32(spread, hi, static_cast<uint32_t>(bal >> 32), 0xDE);
+        lo = __builtin_amdgcn_bitop3_b32(spread[i], lo, static_cast<uint32_t>(bal[i]), 0xDE);
+        hi = __builtin_amdgcn_bitop3_b32(spread[i], hi, static_cast<uint32_t>(bal[i] >> 32), 0xDE);
     }
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
