@@ -419,6 +419,32 @@ def test_scan_strategy_rejects_unknown():
     assert lrs.radix_sort_set_scan_strategy("lookback") in ("lookback", "reduce-then-scan")
 
 
+def test_two_sorts_in_flight_on_two_streams():
+    # independent workspaces: tickets, look-back words and histograms never mix
+    n = 3_000_017
+    a = workloads.random_u32(9600, n)
+    b = workloads.random_u32(9601, n) & workloads.random_u32(9602, n)
+    va = np.arange(n, dtype=np.uint32)
+    ka, kb, vt = to_gpu(a), to_gpu(b), to_gpu(va)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            oa = lrs.radix_sort_pairs(ka, vt, 0, 32, 8)
+        with torch.cuda.stream(s2):
+            ob = lrs.radix_sort_pairs(kb, vt, 0, 32, 4)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    ea = oracle.radix_sort_pairs(a, va, 0, 32, 8)
+    eb = oracle.radix_sort_pairs(b, va, 0, 32, 4)
+    for (oa, ob) in outs:
+        assert_same(to_np_u32(oa[0]), ea[0], "stream 1 keys")
+        assert_same(to_np_u32(oa[1]), ea[1], "stream 1 values")
+        assert_same(to_np_u32(ob[0]), eb[0], "stream 2 keys")
+        assert_same(to_np_u32(ob[1]), eb[1], "stream 2 values")
+
+
 # ------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("n", [1000, 300_000])
