@@ -488,3 +488,129 @@ def test_hip_graph_capture_and_replay(n):
         torch.cuda.synchronize()
         assert_same(to_np_u32(ko2), ek, f"eager {rep} keys")
         assert_same(to_np_u32(vo2), ev, f"eager {rep} values")
+
+
+def _replay_checked(make_inputs, load, run, expect, compare, reps=3):
+    """Capture run() once, then for each rep: load fresh inputs into the captured
+    buffers, replay, compare with the oracle, and run the same call eagerly
+    (with its own outputs) between replays."""
+    load(make_inputs(0))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = run()
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        inputs = make_inputs(rep + 1)
+        load(inputs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        exp = expect(inputs)
+        compare(captured, exp, f"replay {rep}")
+        eager = run(fresh=True)
+        torch.cuda.synchronize()
+        compare(eager, exp, f"eager {rep}")
+
+
+def test_hip_graph_segmented_rows_multi_tile():
+    """Rows longer than one workgroup's tile take the histogram + look-back
+    launches; the captured chain must replay correctly on new rows."""
+    rows, n = 6, 20_011
+    x = torch.empty((rows, n), dtype=torch.float16, device="cuda")
+    vo = torch.empty_like(x)
+    io = torch.empty((rows, n), dtype=torch.int64, device="cuda")
+    ws = torch.empty(max(1, lrs.segmented_row_sort_workspace_size(rows, n, 4)), dtype=torch.uint8, device="cuda")
+
+    def make_inputs(rep):
+        v = workloads.normal_f64(9700 + rep, rows * n).astype(np.float16)
+        v[:: 3 + rep] = np.round(v[:: 3 + rep])  # ties
+        return v.view(np.uint16).reshape(rows, n)
+
+    def load(u):
+        x.copy_(torch.from_numpy(u.view(np.int16).copy()).cuda().view(torch.float16))
+
+    def run(fresh=False):
+        if fresh:
+            return lrs.segmented_row_sort(x, True, 4)
+        return lrs.segmented_row_sort(x, True, 4, values_out=vo, indices_out=io, workspace=ws)
+
+    def compare(got, exp, what):
+        gv = got[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        gi = got[1].cpu().numpy()
+        assert np.array_equal(gv, exp[0]), f"{what}: values differ"
+        assert np.array_equal(gi, exp[1]), f"{what}: indices differ"
+
+    _replay_checked(make_inputs, load, run, lambda u: oracle.segmented_row_sort(u, True, 4), compare)
+
+
+def test_hip_graph_typed_f64_pairs():
+    """64-bit keys (eight 8-bit passes through the 64-bit sweep) in a graph."""
+    n = 1_200_007
+    k = torch.empty(n, dtype=torch.float64, device="cuda")
+    v = torch.empty(n, dtype=torch.int32, device="cuda")
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, lrs.radix_sort_typed_workspace_size(n, "f64", 0, 64, 8, True)),
+                     dtype=torch.uint8, device="cuda")
+
+    def make_inputs(rep):
+        x = workloads.normal_f64(9800 + rep, n)
+        x[:: 5 + rep] = np.round(x[:: 5 + rep])
+        return x.view(np.uint64).copy(), workloads.random_u32(9850 + rep, n)
+
+    def load(inp):
+        k.copy_(torch.from_numpy(inp[0].view(np.float64)).cuda())
+        v.copy_(to_gpu(inp[1]))
+
+    def run(fresh=False):
+        if fresh:
+            return lrs.radix_sort_pairs_typed(k, v, False)
+        return lrs.radix_sort_pairs_typed(k, v, False, keys_out=ko, values_out=vo, workspace=ws)
+
+    def compare(got, exp, what):
+        gk = got[0].view(torch.int64).cpu().numpy().view(np.uint64)
+        assert np.array_equal(gk, exp[0]), f"{what}: keys differ"
+        assert_same(to_np_u32(got[1]), exp[1], f"{what}: values")
+
+    _replay_checked(make_inputs, load, run,
+                    lambda inp: oracle.radix_sort_typed(inp[0], inp[1], "f64", False, 0, 64, 8), compare)
+
+
+def test_hip_graph_reduce_then_scan():
+    """The reduce-then-scan launches (clear, histogram, and per pass count, scan
+    and sweep) captured while that strategy is selected."""
+    n = 2_000_003
+    kin = torch.empty(n, dtype=torch.int32, device="cuda")
+    vin, kout, vout = torch.empty_like(kin), torch.empty_like(kin), torch.empty_like(kin)
+    ws = torch.empty(max(1, lrs.radix_sort_workspace_size(n, 0, 32, 4, True)), dtype=torch.uint8, device="cuda")
+
+    def make_inputs(rep):
+        keys = workloads.random_u32(9900 + rep, n)
+        if rep == 2:
+            keys &= workloads.random_u32(9950, n) & workloads.random_u32(9951, n)
+        return keys, np.arange(n, dtype=np.uint32)
+
+    def load(inp):
+        kin.copy_(to_gpu(inp[0]))
+        vin.copy_(to_gpu(inp[1]))
+
+    def run(fresh=False):
+        if fresh:
+            return lrs.radix_sort_pairs(kin, vin, 0, 32, 4)
+        return lrs.radix_sort_pairs(kin, vin, 0, 32, 4, keys_out=kout, values_out=vout, workspace=ws)
+
+    def compare(got, exp, what):
+        assert_same(to_np_u32(got[0]), exp[0], f"{what} keys")
+        assert_same(to_np_u32(got[1]), exp[1], f"{what} values")
+
+    previous = lrs.radix_sort_set_scan_strategy("reduce-then-scan")
+    try:
+        _replay_checked(make_inputs, load, run, lambda inp: oracle.radix_sort_pairs(inp[0], inp[1], 0, 32, 4),
+                        compare)
+    finally:
+        lrs.radix_sort_set_scan_strategy(previous)
