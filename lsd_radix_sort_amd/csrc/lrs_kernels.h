@@ -597,18 +597,31 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
         for (int i = 0; i < (ITEMS + 3) / 4; ++i) slot_digits[i] = 0u;
         const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
+        // Without the bounds select (full tiles) the loop has no branches and
+        // all of a thread's slot reads can be in flight at once.  Only keys-only
+        // sorts take that copy: with a payload it measured no faster.
+        auto keys_out = [&](auto partial) {
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            const uint32_t k = i * BLOCK + tid;
-            const Word v = s_buf[k];
-            const uint32_t d = digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
-            if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
-            const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
-            if constexpr (kWide) {
-                if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
-            } else {
-                BufIO<Stored>::store(kout_rsrc, dst, v);
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t k = i * BLOCK + tid;
+                const Word v = s_buf[k];
+                const uint32_t d = digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
+                if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
+                uint32_t dst;
+                if constexpr (decltype(partial)::value) dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
+                else dst = s_goff[d] + k;
+                if constexpr (kWide) {
+                    if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
+                } else {
+                    BufIO<Stored>::store(kout_rsrc, dst, v);
+                }
             }
+        };
+        if constexpr (PK == kPayNone) {
+            if (valid == TILE) keys_out(std::false_type{});
+            else keys_out(std::true_type{});
+        } else {
+            keys_out(std::true_type{});
         }
 
         if constexpr (PK != kPayNone) {
