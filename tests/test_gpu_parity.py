@@ -129,6 +129,27 @@ def test_mid_tile_configuration(b, dist):
     assert_same(gpu_keys(keys, 0, 32, b), ek, "keys only")
 
 
+@pytest.mark.parametrize("n", [15_360 * 260, 15_360 * 260 + 1, 8_192 * 300, 8_192 * 300 + 1])
+def test_exact_tile_multiples(n):
+    # every tile full (each tile takes the copy of the loops without bounds
+    # tests), and the same plus a last tile holding one element
+    keys = workloads.random_u32(4600 + n % 7, n)
+    keys[::3] &= 0xFF00FF00  # ties in alternate digits
+    vals = workloads.random_u32(4700, n)
+    log(f"exact tile multiple n={n}")
+    ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
+    gk, gv = gpu_pairs(keys, vals, 0, 32, 8)
+    assert_same(gk, ek, "keys")
+    assert_same(gv, ev, "values")
+    assert_same(gpu_keys(keys, 0, 32, 8), ek, "keys only")
+    ek4 = oracle.radix_sort_keys(keys, 4, 28, 4)
+    assert_same(gpu_keys(keys, 4, 28, 4), ek4, "keys only, bits 4-27, b=4")
+    ei, _ = oracle.radix_sort_typed(keys, None, "i32", False)
+    gi = lrs.radix_sort_keys_typed(to_gpu(keys))  # int32 tensor: signed keys
+    torch.cuda.synchronize()
+    assert_same(to_np_u32(gi), ei, "int32 keys only")
+
+
 def test_pass_by_pass_states():
     # the state after p passes is the stable sort by the low p*b bits of the window
     n = 300_001
