@@ -11,7 +11,8 @@ Prints one JSON line.
 
 Other workloads (same line format, for the record): c1_keys_1k_4bit,
 c2_keys_4m_4bit, c2_keys_4m_8bit, c3_pairs_2p28_and3, c4_fp16_1024x65536_asc,
-c5_bf16_4096x4096_desc.
+c5_bf16_4096x4096_desc, f32_pairs_2p28_desc, i32_keys_2p28_asc,
+f64_pairs_2p27_asc.
 
 roofline: the dominant kernel is the sweep (one LSD pass).  achieved = the
 algorithmic bytes of the sweep launches of one sort (pairs: 16 B per pair per

@@ -1,0 +1,53 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the algorithmic byte
+counts the roofline divides by, and the workload table."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_headline_sweep_bytes():
+    # 4 passes, each reading and writing a 4-byte key and a 4-byte value per pair
+    w = bench.WORKLOADS[bench.HEADLINE]
+    assert (w["kind"], w["n"], w["end_bit"], w["b"]) == ("pairs", 1 << 28, 32, 8)
+    assert bench.sweep_bytes(w) == 4 * 16 * (1 << 28)
+
+
+def test_keys_only_sweep_bytes():
+    assert bench.sweep_bytes(bench.WORKLOADS["c2_keys_4m_4bit"]) == 8 * 8 * (1 << 22)
+    assert bench.sweep_bytes(bench.WORKLOADS["c2_keys_4m_8bit"]) == 4 * 8 * (1 << 22)
+    assert bench.sweep_bytes(bench.WORKLOADS["i32_keys_2p28_asc"]) == 4 * 8 * (1 << 28)
+
+
+def test_wide_key_sweep_bytes():
+    # 8-byte keys with a 4-byte value: 24 B per pair per pass, 8 passes of 8 bits
+    assert bench.sweep_bytes(bench.WORKLOADS["f64_pairs_2p27_asc"]) == 8 * 24 * (1 << 27)
+
+
+def test_row_sort_bytes():
+    # fp16 rows, 4 passes: 2 in + 2+4 out, then 6 + 6 twice, then 6 in + 2+8 out = 48 B per element
+    w = bench.WORKLOADS["c4_fp16_1024x65536_asc"]
+    assert bench.sweep_bytes(w) == 48 * 1024 * 65536
+    # whole-row sort: the pattern in, the pattern and an int64 index out
+    assert bench.resident_bytes(bench.WORKLOADS["c5_bf16_4096x4096_desc"]) == 12 * 4096 * 4096
+    assert bench.resident_bytes(bench.WORKLOADS["c1_keys_1k_4bit"]) == 8 * 1024
+
+
+def test_workload_table_is_complete():
+    for name, w in bench.WORKLOADS.items():
+        assert w["kind"] in ("keys", "pairs", "rows") and w["b"] in (1, 2, 4, 8), name
+        assert w["desc"], name
+    assert set(bench.MEASURED_SWEEP_TRAFFIC) <= set(bench.WORKLOADS)
+    # the traffic on record is within a few percent of the headline's algorithmic bytes per launch
+    ratio = bench.MEASURED_SWEEP_TRAFFIC[bench.HEADLINE] / (16 * (1 << 28))
+    assert 1.0 <= ratio < 1.1
