@@ -137,7 +137,7 @@ struct Plan {
     int tile_cfg = 0;
     uint32_t tiles_per_row = 0;
     uint64_t num_tiles = 0;
-    bool wide_status = false;       // 64-bit look-back words, 64-bit stores (row_len >= 2^29)
+    bool wide_status = false;       // 64-bit look-back words and store addresses (see make_plan)
     uint32_t hist_chunks_per_row = 0;
     // workspace layout (byte offsets)
     uint64_t off_hist = 0, hist_words = 0;
@@ -162,7 +162,13 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.tile_cfg = choose_tile_cfg(rows, row_len, key64);
     p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, tile_cfg_of(key64, p.tile_cfg).tile));
     p.num_tiles = rows * p.tiles_per_row;
-    p.wide_status = row_len >= (1ull << 29);
+    // A row needs the wide sweep (64-bit look-back words, 64-bit store
+    // addresses) once its byte offsets pass what a 32-bit buffer offset
+    // reaches (2^32 bytes) or its counts pass the 30-bit count of a 32-bit
+    // look-back word: from 2^30 elements of 4 bytes, and from 2^29 for 8-byte
+    // keys and for row sorts (int64 index out).
+    const uint64_t widest = (kind == 2) ? 8 : static_cast<uint64_t>(key_bytes);
+    p.wide_status = row_len * widest >= (1ull << 32) || row_len >= (1ull << 30);
 
     // histogram: about kHistTargetBlocks workgroups in all, at least
     // kHistMinChunk keys each
@@ -265,7 +271,8 @@ hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t grid,
     constexpr bool k64 = sizeof(typename KeyTraits<KK>::Stored) == 8;
     constexpr TileCfg c0 = tile_cfg_of(k64, 0), c1 = tile_cfg_of(k64, 1), c2 = tile_cfg_of(k64, 2);
     // 64-bit look-back words (and 64-bit store addressing) only occur for rows
-    // of 2^29 or more elements, which always take the largest tile.
+    // of 2^29 or more elements (2^30 for 4-byte keys), which always take the
+    // largest tile.
     if (wide)
         launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint64_t, PART>(a, grid, s);
     else if (cfg == 2)

@@ -248,11 +248,12 @@ def _u32_to_i64(t):
 
 
 @pytest.mark.timeout(600)
-def test_row_of_2p29_and_more_elements():
-    """A row of at least 2^29 elements takes 64-bit look-back words and 64-bit
-    store addresses; compared element for element with the oracle."""
-    n = (1 << 29) + 12_345
-    log(f"wide row n={n}: generating")
+@pytest.mark.parametrize("n", [(1 << 29) + 12_345, (1 << 30) + 12_345])
+def test_rows_past_2p29_and_2p30_elements(n):
+    """Beyond 2^29 u32 pairs the byte offsets of the 32-bit sweep pass 2^31;
+    from 2^30 the row takes 64-bit look-back words and 64-bit store
+    addresses.  Compared element for element with the oracle."""
+    log(f"long row n={n}: generating")
     # a seeded 2^20-key block repeated, each copy scrambled by its index
     block = workloads.random_u32(4800, 1 << 20)
     keys = np.tile(block, n // block.size + 1)[:n]
@@ -260,14 +261,14 @@ def test_row_of_2p29_and_more_elements():
     keys[1::2] &= np.uint32(0xF0F0F0F0)  # half the keys: ties in every digit
     vals = np.arange(n, dtype=np.uint32)
     kt, vt = to_gpu(keys), to_gpu(vals)
-    log("wide row: sorting on the GPU")
+    log("long row: sorting on the GPU")
     ko, vo = lrs.radix_sort_pairs(kt, vt, 0, 32, 8)
     torch.cuda.synchronize()
     del kt, vt
     gk, gv = to_np_u32(ko), to_np_u32(vo)
     del ko, vo
     torch.cuda.empty_cache()
-    log("wide row: oracle")
+    log("long row: oracle")
     ek, ev = oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
     assert_same(gk, ek, "keys")
     assert_same(gv, ev, "values")
