@@ -599,7 +599,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
         // Without the bounds select (full tiles) the loop has no branches and
         // all of a thread's slot reads can be in flight at once.  Only keys-only
-        // sorts take that copy: with a payload it measured no faster.
+        // sorts take that copy: with a payload it measured slower.
         auto keys_out = [&](auto partial) {
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
