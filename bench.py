@@ -12,7 +12,7 @@ Prints one JSON line.
 Other workloads (same line format, for the record): c1_keys_1k_4bit,
 c2_keys_4m_4bit, c2_keys_4m_8bit, c3_pairs_2p28_and3, c4_fp16_1024x65536_asc,
 c5_bf16_4096x4096_desc, f32_pairs_2p28_desc, i32_keys_2p28_asc,
-f64_pairs_2p27_asc.
+f64_pairs_2p27_asc, u32_pairs_2p29_uniform, u32_pairs_2p30_uniform.
 
 roofline: the dominant kernel is the sweep (one LSD pass).  achieved = the
 algorithmic bytes of the sweep launches of one sort (pairs: 16 B per pair per
@@ -72,6 +72,12 @@ WORKLOADS = {
                                      "descending, 8-bit digits, 4 passes"),
     "i32_keys_2p28_asc": dict(kind="keys", typed="i32", descending=False, n=1 << 28, end_bit=32, b=8,
                               desc="2^28 uniform int32 keys, keys only, ascending, 8-bit digits, 4 passes"),
+    "u32_pairs_2p29_uniform": dict(kind="pairs", n=1 << 29, end_bit=32, b=8, dist="uniform",
+                                   desc="2^29 u32 key + u32 value pairs (value = original index), uniform keys, "
+                                        "8-bit digits, 4 passes (32-bit sweep; byte offsets past 2^31)"),
+    "u32_pairs_2p30_uniform": dict(kind="pairs", n=1 << 30, end_bit=32, b=8, dist="uniform",
+                                   desc="2^30 u32 key + u32 value pairs (value = original index), uniform keys, "
+                                        "8-bit digits, 4 passes (64-bit look-back words and store addresses)"),
     "f64_pairs_2p27_asc": dict(kind="pairs", typed="f64", descending=False, n=1 << 27, end_bit=64, b=8,
                                key_bytes=8, desc="2^27 fp64 N(0,1) keys + u32 value pairs (value = original "
                                                  "index), ascending, 8-bit digits, 8 passes"),
