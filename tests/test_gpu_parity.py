@@ -248,11 +248,13 @@ def _u32_to_i64(t):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("n", [(1 << 29) + 12_345, (1 << 30) + 12_345])
-def test_rows_past_2p29_and_2p30_elements(n):
-    """Beyond 2^29 u32 pairs the byte offsets of the 32-bit sweep pass 2^31;
-    from 2^30 the row takes 64-bit look-back words and 64-bit store
-    addresses.  Compared element for element with the oracle."""
+@pytest.mark.parametrize("n,strategy", [((1 << 29) + 12_345, "lookback"), ((1 << 29) + 12_345, "reduce-then-scan"),
+                                        ((1 << 30) + 12_345, "lookback")])
+def test_rows_past_2p29_and_2p30_elements(n, strategy):
+    """Beyond 2^29 u32 pairs the byte offsets of the 32-bit sweep pass 2^31
+    (with either scan strategy); from 2^30 the row takes 64-bit look-back
+    words and 64-bit store addresses.  Compared element for element with the
+    oracle."""
     log(f"long row n={n}: generating")
     # a seeded 2^20-key block repeated, each copy scrambled by its index
     block = workloads.random_u32(4800, 1 << 20)
@@ -261,9 +263,13 @@ def test_rows_past_2p29_and_2p30_elements(n):
     keys[1::2] &= np.uint32(0xF0F0F0F0)  # half the keys: ties in every digit
     vals = np.arange(n, dtype=np.uint32)
     kt, vt = to_gpu(keys), to_gpu(vals)
-    log("long row: sorting on the GPU")
-    ko, vo = lrs.radix_sort_pairs(kt, vt, 0, 32, 8)
-    torch.cuda.synchronize()
+    log(f"long row: sorting on the GPU ({strategy})")
+    previous = lrs.radix_sort_set_scan_strategy(strategy)
+    try:
+        ko, vo = lrs.radix_sort_pairs(kt, vt, 0, 32, 8)
+        torch.cuda.synchronize()
+    finally:
+        lrs.radix_sort_set_scan_strategy(previous)
     del kt, vt
     gk, gv = to_np_u32(ko), to_np_u32(vo)
     del ko, vo
