@@ -17,24 +17,49 @@
 #include <vector>
 
 #include "../../include/lsd_radix_sort.h"
-#include "lrs_kernels.h"
+#include "lrs_launch.h"
 
 namespace lrs {
+
+// --------------------------------------------------- utility kernels
+
+// Zero `words` u32 words at each of up to three regions.
+struct ClearArgs {
+    uint32_t *p[3];
+    uint64_t words[3];
+};
+
+__global__ __launch_bounds__(kBlock) void clear_kernel(ClearArgs a) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (int r = 0; r < 3; ++r) {
+        uint32_t *p = a.p[r];
+        if (p == nullptr) continue;
+        const uint64_t n = a.words[r];
+        const uint64_t n4 = n / 4;  // regions are 16-byte aligned
+        uint4 *p4 = reinterpret_cast<uint4 *>(p);
+        for (uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n4; i += stride)
+            p4[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (uint64_t i = n4 * 4 + blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n; i += stride)
+            p[i] = 0u;
+    }
+}
+
+// Plain streaming copy: one 16-byte word per thread and a grid that covers the
+// buffer once (a grid-stride loop only past 2^20 workgroups).  On MI355X this
+// shape moves about 6.1 TB/s; unrolled or grid-stride shapes with more bytes
+// per thread in flight lose a quarter of that or more.
+__global__ __launch_bounds__(kBlock) void copy_kernel(const uint4 *src, uint4 *dst, uint64_t n16,
+                                                      const uint8_t *src_tail, uint8_t *dst_tail,
+                                                      uint32_t tail) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+    if (blockIdx.x == 0 && threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
+}
+
+
 namespace {
 
-// Sweep tile shapes (threads x keys per thread).  Long rows use the largest;
-// shorter inputs a smaller one so the grid still has several tiles per CU and
-// little of the last tile of each row is padding.
-struct TileCfg {
-    int block;
-    int items;
-    uint64_t tile;
-};
-constexpr TileCfg kTileCfgs[3] = {
-    {256, 16, 4096}, {512, 16, 8192}, {kSweepBlock, LRS_SWEEP_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_ITEMS}};
-// 64-bit keys take twice the registers and LDS per key: half the keys per tile.
-constexpr TileCfg kTileCfgs64[3] = {{256, 8, 2048}, {512, 8, 4096}, {512, 16, 8192}};
-constexpr TileCfg tile_cfg_of(bool key64, int c) { return key64 ? kTileCfgs64[c] : kTileCfgs[c]; }
 #ifndef LRS_MIN_TILES
 #define LRS_MIN_TILES 256
 #endif
@@ -224,111 +249,11 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 // ------------------------------------------------------------ launches
 
-template <int B, int KK>
-hipError_t launch_hist_b(const HistArgs &a, uint32_t blocks, hipStream_t s) {
-    histogram_kernel<B, KK><<<blocks, kHistBlock, 0, s>>>(a);
-    return hipGetLastError();
-}
-
-template <int KK>
-hipError_t launch_hist(int b, const HistArgs &a, uint32_t blocks, hipStream_t s) {
-    switch (b) {
-        case 1: return launch_hist_b<1, KK>(a, blocks, s);
-        case 2: return launch_hist_b<2, KK>(a, blocks, s);
-        case 4: return launch_hist_b<4, KK>(a, blocks, s);
-        default: return launch_hist_b<8, KK>(a, blocks, s);
-    }
-}
-
-// Digit-group matching used by the sweep: LRS_MATCH_DEFAULT unless the
-// environment variable LRS_MATCH is "ballot" or "lds" (both are complete
-// implementations; the switch exists to compare them).
-#ifndef LRS_MATCH_DEFAULT
-#define LRS_MATCH_DEFAULT 0  // kMatchBallot
-#endif
-int match_kind() {
-    static const int kind = [] {
-        const char *e = std::getenv("LRS_MATCH");
-        if (e != nullptr && std::strcmp(e, "ballot") == 0) return int(kMatchBallot);
-        if (e != nullptr && std::strcmp(e, "lds") == 0) return int(kMatchLds);
-        return int(LRS_MATCH_DEFAULT);
-    }();
-    return kind;
-}
-
-// `grid` workgroups: one per tile (look-back), or one per partition (PART).
-template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, bool PART>
-void launch_sweep_cfg(const SweepArgs &a, uint64_t grid_size, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(grid_size));
-    if (PART || match_kind() == kMatchBallot)
-        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchBallot, PART><<<grid, BLOCK, 0, s>>>(a);
-    else
-        sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, kMatchLds, false><<<grid, BLOCK, 0, s>>>(a);
-}
-
-template <int B, int KK, int PK, bool PART>
-hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s) {
-    constexpr bool k64 = sizeof(typename KeyTraits<KK>::Stored) == 8;
-    constexpr TileCfg c0 = tile_cfg_of(k64, 0), c1 = tile_cfg_of(k64, 1), c2 = tile_cfg_of(k64, 2);
-    // 64-bit look-back words (and 64-bit store addressing) only occur for rows
-    // of 2^29 or more elements (2^30 for 4-byte keys), which always take the
-    // largest tile.
-    if (wide)
-        launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint64_t, PART>(a, grid, s);
-    else if (cfg == 2)
-        launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint32_t, PART>(a, grid, s);
-    else if (cfg == 1)
-        launch_sweep_cfg<B, c1.items, c1.block, KK, PK, uint32_t, PART>(a, grid, s);
-    else
-        launch_sweep_cfg<B, c0.items, c0.block, KK, PK, uint32_t, PART>(a, grid, s);
-    return hipGetLastError();
-}
-
-template <int KK, int PK, bool PART = false>
-hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s) {
-    switch (b) {
-        case 1: return launch_sweep_b<1, KK, PK, PART>(a, cfg, wide, grid, s);
-        case 2: return launch_sweep_b<2, KK, PK, PART>(a, cfg, wide, grid, s);
-        case 4: return launch_sweep_b<4, KK, PK, PART>(a, cfg, wide, grid, s);
-        default: return launch_sweep_b<8, KK, PK, PART>(a, cfg, wide, grid, s);
-    }
-}
-
-template <int KK>
-hipError_t launch_partition_counts(int b, const PartArgs &pa, hipStream_t s) {
-    const dim3 grid(pa.partitions);
-    switch (b) {
-        case 1: partition_count_kernel<1, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<1><<<1, 256, 0, s>>>(pa); break;
-        case 2: partition_count_kernel<2, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<2><<<1, 256, 0, s>>>(pa); break;
-        case 4: partition_count_kernel<4, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<4><<<1, 256, 0, s>>>(pa); break;
-        default: partition_count_kernel<8, KK><<<grid, kHistBlock, 0, s>>>(pa); partition_scan_kernel<8><<<1, 256, 0, s>>>(pa); break;
-    }
-    return hipGetLastError();
-}
-
-template <int B, int KK, int PK>
-hipError_t launch_resident_b(const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s) {
-    // one workgroup per row; the smallest shape that holds the row
-    const dim3 grid(static_cast<uint32_t>(rows));
-    if (row_len <= 1024)
-        resident_sort_kernel<B, 4, 256, KK, PK><<<grid, 256, 0, s>>>(a);
-    else if (row_len <= 4096)
-        resident_sort_kernel<B, 16, 256, KK, PK><<<grid, 256, 0, s>>>(a);
-    else
-        resident_sort_kernel<B, 16, 512, KK, PK><<<grid, 512, 0, s>>>(a);
-    return hipGetLastError();
-}
-
+// Whole-row resident sort, timed as kind 4.
 template <int KK, int PK>
-hipError_t launch_resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s) {
+hipError_t resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s) {
     TimedLaunch t(4, s);
-    hipError_t e;
-    switch (b) {
-        case 1: e = launch_resident_b<1, KK, PK>(a, rows, row_len, s); break;
-        case 2: e = launch_resident_b<2, KK, PK>(a, rows, row_len, s); break;
-        case 4: e = launch_resident_b<4, KK, PK>(a, rows, row_len, s); break;
-        default: e = launch_resident_b<8, KK, PK>(a, rows, row_len, s); break;
-    }
+    const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, s);
     t.done();
     return e;
 }
@@ -523,9 +448,9 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
         r.flip_neg = flip_neg;
         hipError_t e;
         if (kk == kKeyU32)
-            e = pairs ? launch_resident<kKeyU32, kResU32>(b, r, 1, n, s) : launch_resident<kKeyU32, kResNone>(b, r, 1, n, s);
+            e = pairs ? resident<kKeyU32, kResU32>(b, r, 1, n, s) : resident<kKeyU32, kResNone>(b, r, 1, n, s);
         else
-            e = pairs ? launch_resident<kKeyX32, kResU32>(b, r, 1, n, s) : launch_resident<kKeyX32, kResNone>(b, r, 1, n, s);
+            e = pairs ? resident<kKeyX32, kResU32>(b, r, 1, n, s) : resident<kKeyX32, kResNone>(b, r, 1, n, s);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -553,12 +478,12 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX32, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX32, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -613,12 +538,12 @@ int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX64, kPayU32>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
             src_v = dv;
         } else {
-            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX64, kPayNone>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
+                                : launch_sweep<kKeyX64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -741,7 +666,7 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
         r.begin_bit = 0;
         r.end_bit = 16;
         r.flip = flip;
-        const hipError_t e = launch_resident<kKeyF16, kResIndex>(digit_bits, r, rows, n, s);
+        const hipError_t e = resident<kKeyF16, kResIndex>(digit_bits, r, rows, n, s);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -764,15 +689,15 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
         if (pass == 0) {
             a.vals_in = nullptr;
             a.vals_out = idx[0];
-            e = launch_sweep<kKeyF16, kPayIdxFirst>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayIdxFirst, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         } else if (pass + 1 < p.passes) {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx[pass & 1];
-            e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         } else {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx_out;
-            e = launch_sweep<kKeyF16, kPayIdxLast>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = launch_sweep<kKeyF16, kPayIdxLast, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -817,7 +742,7 @@ int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, ui
         r.begin_bit = 0;
         r.end_bit = 16;
         r.flip = flip;
-        const hipError_t e = launch_resident<kKeyF16, kResU32>(digit_bits, r, rows, n, s);
+        const hipError_t e = resident<kKeyF16, kResU32>(digit_bits, r, rows, n, s);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -838,7 +763,7 @@ int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, ui
         a.vals_in = src_p;
         a.vals_out = dp;
         TimedLaunch t(2, s);
-        const hipError_t e = launch_sweep<kKeyF16, kPayU32>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+        const hipError_t e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;

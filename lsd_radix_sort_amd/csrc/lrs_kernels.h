@@ -220,11 +220,7 @@ __device__ inline uint32_t count_below(uint64_t m) {
 }
 
 // This lane's rank among the lanes of its digit group, and the group's size,
-// from the group's member mask (LDS matching) or its mismatch mask (ballots).
-__device__ inline void group_rank_from_members(uint64_t members, uint32_t &below, uint32_t &size) {
-    below = count_below(members);
-    size = static_cast<uint32_t>(__popcll(members));
-}
+// from the group's mismatch mask.
 __device__ inline void group_rank_from_mismatch(uint64_t mismatch, int lane, uint32_t &below, uint32_t &size) {
     below = static_cast<uint32_t>(lane) - count_below(mismatch);
     size = 64u - static_cast<uint32_t>(__popcll(mismatch));
@@ -311,9 +307,6 @@ __device__ inline uint32_t take_tile(uint32_t *counters, uint32_t num_tiles) {
     return num_tiles;
 }
 
-// How a wave finds the lanes that share its digit.
-enum MatchKind : int { kMatchBallot = 0, kMatchLds = 1 };
-
 // Workgroup-wide exclusive scan of one value per thread for a BLOCK-thread
 // workgroup.  Every thread must call it.  `tmp` holds BLOCK / 64 words of LDS.
 template <int BLOCK>
@@ -335,8 +328,7 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
 // 1. Load the tile's keys (wave-striped: each wave holds a contiguous run of
 //    the tile and (item, lane) order is input order).
 // 2. Rank stably inside each wave: the lanes sharing a digit are found by
-//    ballots (or by OR-ing lane bits into per-digit masks in LDS); a lane's
-//    rank is the wave's running count of its digit plus the group members at
+//    ballots; a lane's rank is the wave's running count of its digit plus the group members at
 //    lower lanes.
 // 3. Per digit: the tile's count (published at once for the look-back; an
 //    inclusive count for a row's first tile), the digit's start in the tile,
@@ -356,20 +348,17 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
 //
 // At least four waves per SIMD (two 512-thread workgroups per CU): the
 // partition loop would otherwise take 198 registers and halve that.
-template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, int MATCH, bool PART = false>
+template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, bool PART = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void sweep_kernel(SweepArgs a) {
     constexpr uint32_t R = 1u << B;
     constexpr int WAVES = BLOCK / kWave;
     constexpr uint32_t TILE = BLOCK * ITEMS;
     static_assert(BLOCK % kWave == 0 && BLOCK >= static_cast<int>(R), "one thread per digit");
-    static_assert(MATCH != kMatchLds || WAVES * R * 8 <= TILE * 4, "match masks must fit in the tile buffer");
     using Stored = typename KeyTraits<KK>::Stored;
     using Word = typename KeyTraits<KK>::Word;
     using St = Status<W>;
 
-    // s_buf holds the tile in digit order (keys, then payload); during the
-    // ranking its front holds the per-wave digit masks of the LDS matching.
-    // Between writing the keys and the payload out of the same slots, each
+    // s_buf holds the tile in digit order (keys, then payload).  Between writing the keys and the payload out of the same slots, each
     // thread keeps its slots' digits in registers, four to a word.
     __shared__ Word s_buf[TILE];
     uint32_t *const s_pay = reinterpret_cast<uint32_t *>(s_buf);  // the payload's view of the slots
@@ -378,7 +367,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     __shared__ uint32_t s_tmp[WAVES];
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_gave_up;            // a look-back wave stopped waiting
-    auto s_match = reinterpret_cast<unsigned long long (*)[R]>(s_buf);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -386,10 +374,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     // 64-bit look-back words also mark rows too long for 32-bit buffer offsets
     constexpr bool kWide = sizeof(W) == 8;
 
-    static_assert(!PART || MATCH == kMatchBallot, "partition mode ranks by ballots");
     for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
-    if constexpr (MATCH == kMatchLds)
-        for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_match[0][0])[i] = 0ull;
     if (!PART && tid == 0) {
         s_ticket = take_tile(a.tile_counter, a.num_tiles);
         s_gave_up = 0u;
@@ -429,7 +414,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 
         // 2. Stable rank inside the wave; the group's lowest lane advances the
         // running count (and clears the mask).
-        const uint64_t lane_bit = 1ull << lane;
         uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's digit
         // Only a row's last tile has elements past the end, so full tiles take a
         // copy of the loop without the bounds test.
@@ -440,19 +424,11 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                 const uint32_t dig = digit_of<KK>(key[j], a.flip, a.flip_neg, a.shift, a.digit_mask);
                 const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
                 uint32_t below, size;
-                if constexpr (MATCH == kMatchBallot) {
-                    group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
-                } else {
-                    atomicOr(&s_match[wave][d], static_cast<unsigned long long>(lane_bit));
-                    group_rank_from_members(s_match[wave][d], below, size);
-                }
+                group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
                 const uint32_t before = s_cnt[wave][d];
                 rank[j] = (d << 16) | (before + below);
                 pin(rank[j]);
-                if (below == 0u) {
-                    s_cnt[wave][d] = before + size;
-                    if constexpr (MATCH == kMatchLds) s_match[wave][d] = 0ull;
-                }
+                if (below == 0u) s_cnt[wave][d] = before + size;
             }
         };
         if (valid == TILE) rank_items(std::false_type{});
@@ -1022,42 +998,6 @@ __global__ __launch_bounds__(256) void partition_scan_kernel(PartArgs a) {
             }
         }
     }
-}
-
-// ------------------------------------------------------- small utilities
-
-// Zero `words` u32 words at each of up to three regions.
-struct ClearArgs {
-    uint32_t *p[3];
-    uint64_t words[3];
-};
-
-__global__ __launch_bounds__(kBlock) void clear_kernel(ClearArgs a) {
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (int r = 0; r < 3; ++r) {
-        uint32_t *p = a.p[r];
-        if (p == nullptr) continue;
-        const uint64_t n = a.words[r];
-        const uint64_t n4 = n / 4;  // regions are 16-byte aligned
-        uint4 *p4 = reinterpret_cast<uint4 *>(p);
-        for (uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n4; i += stride)
-            p4[i] = make_uint4(0u, 0u, 0u, 0u);
-        for (uint64_t i = n4 * 4 + blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n; i += stride)
-            p[i] = 0u;
-    }
-}
-
-// Plain streaming copy: one 16-byte word per thread and a grid that covers the
-// buffer once (a grid-stride loop only past 2^20 workgroups).  On MI355X this
-// shape moves about 6.1 TB/s; unrolled or grid-stride shapes with more bytes
-// per thread in flight lose a quarter of that or more.
-__global__ __launch_bounds__(kBlock) void copy_kernel(const uint4 *src, uint4 *dst, uint64_t n16,
-                                                      const uint8_t *src_tail, uint8_t *dst_tail,
-                                                      uint32_t tail) {
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t i = blockIdx.x * static_cast<uint64_t>(kBlock) + threadIdx.x; i < n16; i += stride)
-        dst[i] = src[i];
-    if (blockIdx.x == 0 && threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 
 }  // namespace lrs
