@@ -26,6 +26,7 @@ int64 index).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,12 +37,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "c3_pairs_2p28_uniform"
-# HBM bytes per sweep launch of the current sweep kernel on the headline
-# workload (512 x 30 tiles dealt to XCDs in chunks of 16), measured by
-# rocprofv3 FETCH_SIZE and WRITE_SIZE over this benchmark, each scaled by the
-# copy-kernel calibration (x2.0 and x1.0); emptied when the kernel changes
-# until the counters are taken again.
-MEASURED_SWEEP_TRAFFIC = {HEADLINE: 4_451_952_538}
+# Device-code sources whose text fixes the dominant kernels and their launch
+# shapes; their hash ties a counter measurement to the kernel it was taken on.
+KERNEL_SOURCES = ("lsd_radix_sort_amd/csrc/lrs_kernels.h", "lsd_radix_sort_amd/csrc/lrs_launch.h",
+                  "lsd_radix_sort_amd/csrc/lrs_launch_impl.h")
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
+# this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
+# by what the same counter reads for the library's copy kernel of known size;
+# keyed by workload, with the hash of KERNEL_SOURCES the counters were taken
+# on.  A workload whose kernels have changed since reports traffic null.
+MEASURED_TRAFFIC = {}
 
 
 def log(msg):
@@ -110,9 +115,27 @@ def resident_bytes(w) -> int:
     return 12 * w["rows"] * w["cols"]  # 16-bit pattern in; pattern + int64 index out
 
 
+def kernel_sources_sha16() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch of the dominant kernel from the counter runs, or
+    None if there are none for the kernels as they are now."""
+    m = MEASURED_TRAFFIC.get(name)
+    if m is None or m["kernel_sha16"] != kernel_sources_sha16():
+        return None
+    return m["bytes_per_launch"]
+
+
 def cpu_baseline(min_seconds: float = 10.0, max_runs: int = 3):
     """Single-threaded oracle on the headline workload's own input, repeated
-    until at least min_seconds of CPU work (at most max_runs sorts)."""
+    until at least min_seconds of CPU work (at most max_runs sorts); plus the
+    context figure of std::sort on one core over the first 2^24 of its keys."""
     import oracle
     import workloads
 
@@ -124,6 +147,8 @@ def cpu_baseline(min_seconds: float = 10.0, max_runs: int = 3):
         oracle.radix_sort_pairs(keys, vals, 0, 32, 8)
         total += time.perf_counter() - t0
         runs += 1
+    m = 1 << 24
+    std_s = oracle.std_sort_seconds(keys[:m])
     return {
         "value": round(runs * n / total / 1e9, 5),
         "unit": "Gkeys/s",
@@ -132,6 +157,9 @@ def cpu_baseline(min_seconds: float = 10.0, max_runs: int = 3):
         "sample": f"the whole 2^28-pair uniform workload (value = index), 4-pass 8-bit LSD sort by the "
                   f"plain C oracle, single thread, {runs} run(s) in {total:.2f} s",
         "host_cpus": os.cpu_count(),
+        "std_sort_context": {"value": round(m / std_s / 1e9, 5), "unit": "Gkeys/s", "cores": 1,
+                             "sample": f"std::sort of the first 2^24 keys of the same workload (keys only), "
+                                       f"one core, {std_s:.2f} s"},
     }
 
 
@@ -164,8 +192,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lrs.load_library()
-    lrs.radix_sort_set_scan_strategy(args.scan)
     dev = torch.device("cuda:0")
+    timer = lrs.KernelTimer()
+    untimed = lrs.SortOptions(scan=args.scan)
+    timed = lrs.SortOptions(scan=args.scan, timer=timer)
 
     log(f"generating {name}")
     if w["kind"] == "keys" and "typed" in w:
@@ -176,8 +206,9 @@ def main():
         k_out = torch.empty_like(k_in)
         ws = torch.empty(lrs.radix_sort_workspace_size(n_keys, 0, 32, w["b"], False), dtype=torch.uint8, device=dev)
 
-        def step():
-            lrs.radix_sort_keys_typed(k_in, w["descending"], w["typed"], 0, 32, w["b"], out=k_out, workspace=ws)
+        def step(opts):
+            lrs.radix_sort_keys_typed(k_in, w["descending"], w["typed"], 0, 32, w["b"], out=k_out, workspace=ws,
+                                      options=opts)
         copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
     elif w["kind"] == "keys":
         keys = workloads.keys_c1(w["n"]) if w["n"] == 1024 else workloads.keys_c2(w["n"])
@@ -187,8 +218,8 @@ def main():
         ws = torch.empty(max(1, lrs.radix_sort_workspace_size(n_keys, 0, w["end_bit"], w["b"], False)),
                          dtype=torch.uint8, device=dev)
 
-        def step():
-            lrs.radix_sort_keys(k_in, 0, w["end_bit"], w["b"], out=k_out, workspace=ws)
+        def step(opts):
+            lrs.radix_sort_keys(k_in, 0, w["end_bit"], w["b"], out=k_out, workspace=ws, options=opts)
         scratch = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
         copy_pair = (scratch[: 1 << 27], scratch[1 << 27:])
     elif w["kind"] == "pairs" and "typed" in w:
@@ -206,9 +237,9 @@ def main():
         ws = torch.empty(lrs.radix_sort_typed_workspace_size(n_keys, w["typed"], 0, w["end_bit"], w["b"], True),
                          dtype=torch.uint8, device=dev)
 
-        def step():
+        def step(opts):
             lrs.radix_sort_pairs_typed(k_in, v_in, w["descending"], w["typed"], 0, w["end_bit"], w["b"],
-                                       keys_out=k_out, values_out=v_out, workspace=ws)
+                                       keys_out=k_out, values_out=v_out, workspace=ws, options=opts)
         copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
     elif w["kind"] == "pairs":
         keys, vals = workloads.pairs_c3(w["n"], w["dist"])
@@ -220,8 +251,9 @@ def main():
         v_out = torch.empty_like(v_in)
         ws = torch.empty(lrs.radix_sort_workspace_size(n_keys, 0, 32, w["b"], True), dtype=torch.uint8, device=dev)
 
-        def step():
-            lrs.radix_sort_pairs(k_in, v_in, 0, 32, w["b"], keys_out=k_out, values_out=v_out, workspace=ws)
+        def step(opts):
+            lrs.radix_sort_pairs(k_in, v_in, 0, 32, w["b"], keys_out=k_out, values_out=v_out, workspace=ws,
+                                 options=opts)
         copy_pair = (k_in.view(torch.uint8), k_out.view(torch.uint8))
     else:
         bits = workloads.matrix_c4(w["rows"], w["cols"]) if w["dtype"] == "fp16" else workloads.matrix_c5(
@@ -234,8 +266,9 @@ def main():
         ws = torch.empty(lrs.segmented_row_sort_workspace_size(w["rows"], w["cols"], w["b"]), dtype=torch.uint8,
                          device=dev)
 
-        def step():
-            lrs.segmented_row_sort(x, w["descending"], w["b"], values_out=vo, indices_out=io, workspace=ws)
+        def step(opts):
+            lrs.segmented_row_sort(x, w["descending"], w["b"], values_out=vo, indices_out=io, workspace=ws,
+                                   options=opts)
         scratch = io.view(torch.uint8).reshape(-1)
         half = scratch.numel() // 2 // 16 * 16
         copy_pair = (scratch[:half], scratch[half:2 * half])
@@ -243,15 +276,15 @@ def main():
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step()
+        step(untimed)
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    with lrs.KernelTimer() as kt:
+    with timer as kt:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step()
+            step(timed)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -273,9 +306,10 @@ def main():
 
     # copy yardstick: the library's streaming copy kernel between two resident
     # buffers (the 1 GiB key buffers for the 2^28-pair workloads)
-    with lrs.KernelTimer() as ct:
+    copy_opts = lrs.SortOptions(timer=timer)
+    with timer as ct:
         for _ in range(5):
-            lrs.copy_probe(copy_pair[0], copy_pair[1])
+            lrs.copy_probe(copy_pair[0], copy_pair[1], options=copy_opts)
     copy_ms = ct.ms["copy"] / max(ct.launches["copy"], 1)
     copy_gbs = 2 * copy_pair[0].numel() / (copy_ms / 1e3) / 1e9
     log(f"{name}: sort {ms_per_step:.4f} ms/step, {gkeys:.3f} Gkeys/s; {kind} {sweep_ms:.4f} ms/launch "
@@ -303,7 +337,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": MEASURED_SWEEP_TRAFFIC.get(name) if args.scan == "lookback" else None,
+            "traffic": measured_traffic(name) if args.scan == "lookback" else None,
             "kernel": "resident_sort_kernel (whole row, all passes in LDS)" if resident
                       else "sweep_kernel (one LSD pass)",
             "bytes_per_launch": bytes_sort // max(launches_per_sort, 1),

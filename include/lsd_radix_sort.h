@@ -52,7 +52,8 @@ typedef enum lrs_status {
     LRS_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the *_workspace_size() figure */
     LRS_ERR_DTYPE = 7,               /* dtype or key_type not one of the values below */
     LRS_ERR_HIP = 8,                 /* the HIP runtime rejected a launch or query */
-    LRS_ERR_ALIGNMENT = 9            /* a pointer is not aligned as required (see below) */
+    LRS_ERR_ALIGNMENT = 9,           /* a pointer is not aligned as required (see below) */
+    LRS_ERR_OPTION = 10              /* a field of the lrs_options argument has an invalid value */
 } lrs_status;
 
 #define LRS_DTYPE_FP16 0
@@ -72,12 +73,64 @@ typedef enum lrs_status {
 #define LRS_MAX_ROW_LEN ((1ull << 30) - 1ull)
 
 /*
+ * Per-call options.  Every sort entry point (and the workspace-size queries)
+ * takes a `const lrs_options *opts` as its last argument; NULL, or a struct
+ * whose fields are all zero, means the defaults.  Options affect only the call
+ * they are passed to: the library keeps no global settings.
+ *
+ * scan_strategy     How single-row sorts (radix_sort_keys/pairs and the typed
+ *                   forms) find each tile's output offsets (CUDA Handbook
+ *                   ch.16: the scan of the per-block counts; FlagTree PR #1084
+ *                   step 2 compares a status look-back with precomputed offsets):
+ *       LRS_SCAN_LOOKBACK (0, default)  one launch per pass; each tile publishes
+ *           its digit counts and adds up its predecessors' (decoupled look-back).
+ *       LRS_SCAN_REDUCE_THEN_SCAN  three launches per pass: count the digit over
+ *           each of up to 512 partitions of whole tiles, scan those counts into
+ *           start offsets, then sort each partition's tiles in order from them;
+ *           the keys are read once more per pass.  Segmented row sorts and
+ *           64-bit keys always use the look-back.
+ *     The result is identical.  Any other value: LRS_ERR_OPTION.
+ * spin_limit        Bound on how long a sweep tile waits for the counts an
+ *                   earlier tile of its row publishes, in polls of about a
+ *                   microsecond.  A tile that runs out of polls counts its digit
+ *                   over the earlier tiles' keys instead (the same result), so
+ *                   no launch waits forever whatever order the hardware starts
+ *                   workgroups in.  0 = the default, LRS_DEFAULT_SPIN_LIMIT.
+ * prefix_from_keys  Nonzero: no tile waits at all; every tile counts its prefix
+ *                   from the keys (slow; it exists to test that path).
+ * wide_from         0 (default): rows take the sweep with 64-bit look-back words
+ *                   and 64-bit store addresses only where they need it (from
+ *                   2^30 four-byte keys, from 2^29 eight-byte keys or row-sort
+ *                   elements).  Nonzero: rows of at least wide_from elements
+ *                   that are sorted by sweeps (more than 8192 elements) take
+ *                   it as well (a test hook; the result is identical).  Pass
+ *                   the same options to the workspace-size query.
+ * timer             If not NULL, every kernel the call enqueues is bracketed by
+ *                   HIP events on its stream and recorded in this timer (see
+ *                   radix_sort_timer_create).  A timer must not be used by two
+ *                   calls at the same time.
+ */
+#define LRS_SCAN_LOOKBACK 0
+#define LRS_SCAN_REDUCE_THEN_SCAN 1
+#define LRS_DEFAULT_SPIN_LIMIT 65536u
+
+typedef struct lrs_timer lrs_timer;
+
+typedef struct lrs_options {
+    int scan_strategy;
+    uint32_t spin_limit;
+    int prefix_from_keys;
+    uint64_t wide_from;
+    lrs_timer *timer;
+} lrs_options;
+
+/*
  * Bytes of workspace radix_sort_keys (with_values = 0) or radix_sort_pairs
  * (with_values = 1) needs for these arguments.  Returns 0 for arguments the
  * sort would reject, and for n == 0.
  */
 size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int digit_bits,
-                                 int with_values);
+                                 int with_values, const lrs_options *opts);
 
 /*
  * Stable LSD sort of n u32 keys by the bit window [begin_bit, end_bit),
@@ -91,7 +144,7 @@ size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int dig
  */
 int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int begin_bit,
                     int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
-                    void *stream);
+                    void *stream, const lrs_options *opts);
 
 /*
  * As radix_sort_keys, carrying one u32 payload per key: vals_out[i] is the
@@ -101,7 +154,7 @@ int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int
  */
 int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
                      uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
-                     void *workspace, size_t workspace_bytes, void *stream);
+                     void *workspace, size_t workspace_bytes, void *stream, const lrs_options *opts);
 
 /*
  * As segmented_row_sort, but each element carries a caller-supplied u32
@@ -113,7 +166,7 @@ int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t 
  */
 int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out,
                              uint32_t *pay_out, int64_t rows, int64_t n, int dtype, int descending,
-                             int digit_bits, void *workspace, size_t workspace_bytes, void *stream);
+                             int digit_bits, void *workspace, size_t workspace_bytes, void *stream, const lrs_options *opts);
 
 /*
  * Stable LSD sort of n 32- or 64-bit keys of type key_type, ascending or
@@ -141,16 +194,16 @@ int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, ui
  * whole-row resident sort) and the look-back scan strategy.
  */
 size_t radix_sort_typed_workspace_size(uint64_t n, int key_type, int begin_bit, int end_bit, int digit_bits,
-                                       int with_values);
+                                       int with_values, const lrs_options *opts);
 int radix_sort_keys_typed(const void *keys_in, void *keys_out, uint64_t n, int key_type, int descending,
                           int begin_bit, int end_bit, int digit_bits, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          size_t workspace_bytes, void *stream, const lrs_options *opts);
 int radix_sort_pairs_typed(const void *keys_in, const uint32_t *vals_in, void *keys_out, uint32_t *vals_out,
                            uint64_t n, int key_type, int descending, int begin_bit, int end_bit,
-                           int digit_bits, void *workspace, size_t workspace_bytes, void *stream);
+                           int digit_bits, void *workspace, size_t workspace_bytes, void *stream, const lrs_options *opts);
 
 /* Bytes of workspace segmented_row_sort needs; 0 for rejected arguments or empty input. */
-size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits);
+size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits, const lrs_options *opts);
 
 /*
  * Sort each row of a row-major rows x n matrix of fp16 or bf16 values
@@ -171,7 +224,7 @@ size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits
  */
 int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx_out,
                        int64_t rows, int64_t n, int dtype, int descending, int digit_bits,
-                       void *workspace, size_t workspace_bytes, void *stream);
+                       void *workspace, size_t workspace_bytes, void *stream, const lrs_options *opts);
 
 /*
  * The per-pass digit counts of radix_sort_keys' first kernel: all passes'
@@ -182,56 +235,29 @@ int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx
  * accumulated).
  */
 int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit,
-                                int digit_bits, uint32_t *hist_out, void *stream);
+                                int digit_bits, uint32_t *hist_out, void *stream, const lrs_options *opts);
 
 /* Copy `bytes` bytes from src to dst with a plain streaming kernel (the
  * bandwidth yardstick of 100 Days of GPU, Day 35, "Results", the copy row).
- * Both pointers 16-byte aligned, non-overlapping. */
-int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
+ * Both pointers 16-byte aligned, non-overlapping.  Only opts->timer is used. */
+int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream, const lrs_options *opts);
 
 /*
- * Bound on how long a sweep tile waits for the counts an earlier tile of its
- * row publishes (decoupled look-back), in polls of about a microsecond each.
- * When a tile runs out of polls it counts its digit over the keys of the
- * earlier tiles of its row instead, which gives the same result; the bound
- * only guarantees that no launch waits forever, whatever order the hardware
- * starts workgroups in.  0 makes every tile count from the keys (slow; it
- * exists to test that path).  The default is 65536.  Applies to sorts enqueued
- * after the call; returns the previous value.  Not thread-safe.
+ * Kernel timing for measurement (opts->timer).  radix_sort_timer_create
+ * returns a new timer (NULL if host memory runs out); calls given it in their
+ * options bracket each kernel they enqueue with HIP events on their stream.
+ * radix_sort_timer_read waits for the recorded events and reports, per kernel
+ * kind (0 = workspace clear, 1 = digit histogram and the reduce-then-scan
+ * count and scan, 2 = sweep/scatter pass, 3 = copy probe, 4 = whole-row
+ * resident sort), the summed milliseconds and the number of launches in the
+ * two 5-entry arrays (either may be NULL), then empties the timer.  At most
+ * 65536 launches are recorded between reads.  radix_sort_timer_destroy frees
+ * the timer and its events (NULL is a no-op); no call may still be recording
+ * into it.
  */
-uint32_t radix_sort_set_spin_limit(uint32_t polls);
-
-/*
- * How single-row sorts (radix_sort_keys/pairs and the typed forms) get each
- * tile's output offsets (CUDA Handbook ch.16: scan of the per-block counts;
- * FlagTree PR #1084 step 2 compares look-back with precomputed offsets):
- *   LRS_SCAN_LOOKBACK (default)  one launch per pass; each tile publishes its
- *       digit counts and adds up its predecessors' (decoupled look-back).
- *   LRS_SCAN_REDUCE_THEN_SCAN  three launches per pass: count the digit over
- *       each of up to 512 partitions of whole tiles, scan those counts into
- *       start offsets, then sort each partition's tiles in order from them;
- *       the keys are read once more per pass.
- * The result is identical.  Segmented row sorts always use the look-back.
- * Applies to sorts enqueued after the call; returns the previous strategy, or
- * -1 (and changes nothing) for an unknown one.  Not thread-safe.
- */
-#define LRS_SCAN_LOOKBACK 0
-#define LRS_SCAN_REDUCE_THEN_SCAN 1
-int radix_sort_set_scan_strategy(int strategy);
-
-/*
- * Kernel timing for measurement.  After radix_sort_timing_begin(), every
- * kernel the library enqueues is bracketed by HIP events on its stream.
- * radix_sort_timing_end() waits for those events and reports, per kernel kind
- * (0 = workspace clear, 1 = digit histogram (and the reduce-then-scan count
- * and scan), 2 = sweep/scatter pass,
- * 3 = copy probe, 4 = whole-row resident sort), the summed milliseconds and
- * the number of launches, then stops recording.  Arrays have 5 entries.  At
- * most 65536 launches are timed.
- * Not thread-safe; for benchmarking only.
- */
-int radix_sort_timing_begin(void);
-int radix_sort_timing_end(double *ms_by_kind, int *launches_by_kind);
+lrs_timer *radix_sort_timer_create(void);
+int radix_sort_timer_read(lrs_timer *timer, double *ms_by_kind, int *launches_by_kind);
+void radix_sort_timer_destroy(lrs_timer *timer);
 
 /* Static description of a status code; never NULL. */
 const char *radix_sort_status_string(int status);

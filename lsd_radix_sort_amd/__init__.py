@@ -11,8 +11,13 @@ stream.  The entry points have the C ABI's names (include/lsd_radix_sort.h):
     radix_sort_digit_histograms(keys, begin_bit, end_bit, digit_bits)
 
 u32 data is accepted as torch.uint32 or torch.int32 (bit patterns); outputs
-have the input's dtype.  There is no CPU fallback: without the built library or
-a GPU these calls raise.
+have the input's dtype.  Outputs and the workspace may be passed in; each must
+then be a contiguous GPU tensor on the input's device of the exact shape and
+element size the call writes (the workspace: uint8, at least the
+*_workspace_size() bytes), else RadixSortArgumentError is raised before
+anything reaches the library.  Per-call options (scan strategy, look-back wait
+bound, kernel timer) go in a SortOptions; nothing is global.  There is no CPU
+fallback: without the built library or a GPU these calls raise.
 """
 from __future__ import annotations
 
@@ -40,11 +45,9 @@ _SCAN_STRATEGIES = {"lookback": LRS_SCAN_LOOKBACK, "reduce-then-scan": LRS_SCAN_
 STATUS_NAMES = {
     0: "LRS_OK", 1: "LRS_ERR_NULL_POINTER", 2: "LRS_ERR_BIT_RANGE", 3: "LRS_ERR_DIGIT_BITS",
     4: "LRS_ERR_SIZE", 5: "LRS_ERR_ALIASING", 6: "LRS_ERR_WORKSPACE_TOO_SMALL", 7: "LRS_ERR_DTYPE",
-    8: "LRS_ERR_HIP", 9: "LRS_ERR_ALIGNMENT",
+    8: "LRS_ERR_HIP", 9: "LRS_ERR_ALIGNMENT", 10: "LRS_ERR_OPTION",
 }
-_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9}
-
-_lib = None
+_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9, 10}
 
 
 class RadixSortError(RuntimeError):
@@ -54,7 +57,24 @@ class RadixSortError(RuntimeError):
 
 
 class RadixSortArgumentError(RadixSortError, ValueError):
-    pass
+    """An argument the library (or this binding, status None) rejects."""
+
+    def __init__(self, status, what: str):
+        if status is None:
+            self.status = None
+            ValueError.__init__(self, what)
+        else:
+            super().__init__(status, what)
+
+
+class _Options(ctypes.Structure):
+    # mirrors struct lrs_options
+    _fields_ = [("scan_strategy", ctypes.c_int), ("spin_limit", ctypes.c_uint32),
+                ("prefix_from_keys", ctypes.c_int), ("wide_from", ctypes.c_uint64),
+                ("timer", ctypes.c_void_p)]
+
+
+_lib = None
 
 
 def load_library():
@@ -66,38 +86,28 @@ def load_library():
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m lsd_radix_sort_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     P, u64, i64, c_int, szt = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
-    lib.radix_sort_workspace_size.argtypes = [u64, c_int, c_int, c_int, c_int]
-    lib.radix_sort_workspace_size.restype = szt
-    lib.radix_sort_keys.argtypes = [P, P, u64, c_int, c_int, c_int, P, szt, P]
-    lib.radix_sort_keys.restype = c_int
-    lib.radix_sort_pairs.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, P, szt, P]
-    lib.radix_sort_pairs.restype = c_int
-    lib.segmented_row_sort_workspace_size.argtypes = [i64, i64, c_int]
-    lib.segmented_row_sort_workspace_size.restype = szt
-    lib.segmented_row_sort.argtypes = [P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P]
-    lib.segmented_row_sort.restype = c_int
-    lib.segmented_row_sort_pairs.argtypes = [P, P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P]
-    lib.segmented_row_sort_pairs.restype = c_int
-    lib.radix_sort_digit_histograms.argtypes = [P, u64, c_int, c_int, c_int, P, P]
-    lib.radix_sort_digit_histograms.restype = c_int
-    lib.radix_sort_copy_probe.argtypes = [P, P, szt, P]
-    lib.radix_sort_copy_probe.restype = c_int
-    lib.radix_sort_typed_workspace_size.argtypes = [u64, c_int, c_int, c_int, c_int, c_int]
-    lib.radix_sort_typed_workspace_size.restype = szt
-    lib.radix_sort_keys_typed.argtypes = [P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
-    lib.radix_sort_keys_typed.restype = c_int
-    lib.radix_sort_pairs_typed.argtypes = [P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P]
-    lib.radix_sort_pairs_typed.restype = c_int
-    lib.radix_sort_set_scan_strategy.argtypes = [c_int]
-    lib.radix_sort_set_scan_strategy.restype = c_int
-    lib.radix_sort_set_spin_limit.argtypes = [ctypes.c_uint32]
-    lib.radix_sort_set_spin_limit.restype = ctypes.c_uint32
-    lib.radix_sort_timing_begin.argtypes = []
-    lib.radix_sort_timing_begin.restype = c_int
-    lib.radix_sort_timing_end.argtypes = [P, P]
-    lib.radix_sort_timing_end.restype = c_int
-    lib.radix_sort_status_string.argtypes = [c_int]
-    lib.radix_sort_status_string.restype = ctypes.c_char_p
+    O = ctypes.POINTER(_Options)
+    sigs = {
+        "radix_sort_workspace_size": ([u64, c_int, c_int, c_int, c_int, O], szt),
+        "radix_sort_keys": ([P, P, u64, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "radix_sort_pairs": ([P, P, P, P, u64, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "segmented_row_sort_workspace_size": ([i64, i64, c_int, O], szt),
+        "segmented_row_sort": ([P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "segmented_row_sort_pairs": ([P, P, P, P, i64, i64, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "radix_sort_digit_histograms": ([P, u64, c_int, c_int, c_int, P, P, O], c_int),
+        "radix_sort_copy_probe": ([P, P, szt, P, O], c_int),
+        "radix_sort_typed_workspace_size": ([u64, c_int, c_int, c_int, c_int, c_int, O], szt),
+        "radix_sort_keys_typed": ([P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "radix_sort_pairs_typed": ([P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "radix_sort_timer_create": ([], P),
+        "radix_sort_timer_read": ([P, P, P], c_int),
+        "radix_sort_timer_destroy": ([P], None),
+        "radix_sort_status_string": ([c_int], ctypes.c_char_p),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
     _lib = lib
     return lib
 
@@ -113,6 +123,94 @@ def _check(status: int, what: str):
         raise RadixSortError(status, what)
 
 
+def _bad(msg: str):
+    raise RadixSortArgumentError(None, msg)
+
+
+# ------------------------------------------------------------------ options
+
+class KernelTimer:
+    """A library kernel timer (lrs_timer): pass it in SortOptions(timer=...) and
+    every kernel those calls enqueue is bracketed by HIP events on its stream.
+
+    As a context manager, ``ms`` and ``launches`` hold per-kind sums ("clear",
+    "histogram", "sweep", "copy", "resident") after exit; ``read()`` returns
+    them at any time and empties the timer.
+    """
+    KINDS = ("clear", "histogram", "sweep", "copy", "resident")
+
+    def __init__(self):
+        self._lib = load_library()
+        self.handle = self._lib.radix_sort_timer_create()
+        if not self.handle:
+            raise MemoryError("radix_sort_timer_create failed")
+        self.ms, self.launches = {}, {}
+
+    def read(self):
+        ms = (ctypes.c_double * 5)()
+        nl = (ctypes.c_int * 5)()
+        _check(self._lib.radix_sort_timer_read(self.handle, ms, nl), "radix_sort_timer_read")
+        return dict(zip(self.KINDS, list(ms))), dict(zip(self.KINDS, list(nl)))
+
+    def __enter__(self):
+        self.read()  # start empty
+        return self
+
+    def __exit__(self, *exc):
+        self.ms, self.launches = self.read()
+        return False
+
+    def close(self):
+        if self.handle:
+            self._lib.radix_sort_timer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class SortOptions:
+    """Per-call options (struct lrs_options); a call given none uses the defaults.
+
+    scan: "lookback" (default) or "reduce-then-scan" -- how single-row sorts get
+        each tile's output offsets (the result is identical).
+    spin_limit: bound, in polls, on a tile's wait for an earlier tile's counts
+        (None: the library default); past it the tile counts its prefix from the keys.
+    prefix_from_keys: every tile counts its prefix from the keys (tests that path).
+    wide_from: rows of at least this many elements (sorted by sweeps) take the
+        sweep with 64-bit look-back words and store addresses (a test hook).
+    timer: a KernelTimer recording every kernel of the call.
+    """
+
+    def __init__(self, scan: str = "lookback", spin_limit: int | None = None, prefix_from_keys: bool = False,
+                 wide_from: int = 0, timer: KernelTimer | None = None):
+        if scan not in _SCAN_STRATEGIES:
+            _bad(f"scan must be one of {sorted(_SCAN_STRATEGIES)}")
+        if spin_limit is not None and not 1 <= spin_limit <= 0xFFFFFFFF:
+            _bad("spin_limit must be in [1, 2^32)")
+        if not 0 <= wide_from < 1 << 64:
+            _bad("wide_from must be a non-negative 64-bit count")
+        self.timer = timer  # keeps the timer alive while the options are
+        self._c = _Options(_SCAN_STRATEGIES[scan], spin_limit or 0, int(bool(prefix_from_keys)), int(wide_from),
+                           timer.handle if timer is not None else None)
+
+    def _ptr(self):
+        return ctypes.byref(self._c)
+
+
+def _opt(options: SortOptions | None):
+    if options is None:
+        return None
+    if not isinstance(options, SortOptions):
+        _bad("options must be a SortOptions")
+    return options._ptr()
+
+
+# --------------------------------------------------------------- validation
+
 def _stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -121,63 +219,114 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _u32_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+def _gpu_input(t, name: str):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+        _bad(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        _bad(f"{name} must be contiguous")
+
+
+def _u32_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    _gpu_input(t, name)
     if t.dtype not in (torch.uint32, torch.int32):
-        raise ValueError(f"{name} must be uint32 or int32, got {t.dtype}")
-    if t.dim() != 1 or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous 1-D tensor")
+        _bad(f"{name} must be uint32 or int32, got {t.dtype}")
+    if t.dim() != 1:
+        _bad(f"{name} must be a 1-D tensor")
     return t
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+def _same_device(t, name: str, device):
+    if not isinstance(t, torch.Tensor):
+        _bad(f"{name} must be a tensor")
+    if t.device != device:
+        _bad(f"{name} is on {t.device}, the input on {device}")
 
+
+def check_output(t, name: str, device, element_size: int, shape) -> torch.Tensor:
+    """A caller-supplied output must be a contiguous tensor on the input's
+    device with exactly the shape and element size the call writes."""
+    _same_device(t, name, device)
+    if not t.is_contiguous():
+        _bad(f"{name} must be contiguous")
+    if t.element_size() != element_size:
+        _bad(f"{name} must have {element_size}-byte elements, got {t.element_size()}")
+    if tuple(t.shape) != tuple(shape):
+        _bad(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def check_workspace(t, device, nbytes: int) -> torch.Tensor:
+    """A caller-supplied workspace must be a contiguous uint8 tensor on the
+    input's device holding at least nbytes bytes."""
+    _same_device(t, "workspace", device)
+    if t.dtype != torch.uint8 or not t.is_contiguous():
+        _bad("workspace must be a contiguous uint8 tensor")
+    if t.numel() < nbytes:
+        _bad(f"workspace holds {t.numel()} bytes, the call needs {nbytes}")
+    return t
+
+
+def _output(t, name, like: torch.Tensor, element_size=None, shape=None, dtype=None):
+    if t is None:
+        return torch.empty(tuple(like.shape) if shape is None else shape,
+                           dtype=like.dtype if dtype is None else dtype, device=like.device)
+    return check_output(t, name, like.device, like.element_size() if element_size is None else element_size,
+                        like.shape if shape is None else shape)
+
+
+def _workspace(t, nbytes: int, device) -> torch.Tensor:
+    if t is None:
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    return check_workspace(t, device, int(nbytes))
+
+
+# -------------------------------------------------------------------- sorts
 
 def radix_sort_workspace_size(n: int, begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8,
-                              with_values: bool = False) -> int:
-    return int(load_library().radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, int(with_values)))
+                              with_values: bool = False, options: SortOptions | None = None) -> int:
+    return int(load_library().radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, int(with_values),
+                                                        _opt(options)))
 
 
-def segmented_row_sort_workspace_size(rows: int, n: int, digit_bits: int = 8) -> int:
-    return int(load_library().segmented_row_sort_workspace_size(rows, n, digit_bits))
+def segmented_row_sort_workspace_size(rows: int, n: int, digit_bits: int = 8,
+                                      options: SortOptions | None = None) -> int:
+    return int(load_library().segmented_row_sort_workspace_size(rows, n, digit_bits, _opt(options)))
 
 
 def radix_sort_keys(keys: torch.Tensor, begin_bit: int = 0, end_bit: int = 32, digit_bits: int = 8,
-                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    options: SortOptions | None = None) -> torch.Tensor:
     """Stable LSD sort of u32 keys by bits [begin_bit, end_bit); returns the sorted keys."""
     lib = load_library()
     keys = _u32_tensor(keys, "keys")
     n = keys.numel()
-    if out is None:
-        out = torch.empty_like(keys)
-    if workspace is None:
-        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 0), keys.device)
-    _check(lib.radix_sort_keys(_ptr(keys), _ptr(out), n, begin_bit, end_bit, digit_bits,
-                               _ptr(workspace), workspace.numel(), _stream(keys)), "radix_sort_keys")
+    out = _output(out, "out", keys)
+    workspace = _workspace(workspace, lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 0,
+                                                                    _opt(options)), keys.device)
+    _check(lib.radix_sort_keys(_ptr(keys), _ptr(out), n, begin_bit, end_bit, digit_bits, _ptr(workspace),
+                               workspace.numel(), _stream(keys), _opt(options)), "radix_sort_keys")
     return out
 
 
 def radix_sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
                      digit_bits: int = 8, keys_out: torch.Tensor | None = None,
-                     values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                     values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     options: SortOptions | None = None):
     """Stable LSD sort of u32 keys carrying u32 values; returns (keys, values)."""
     lib = load_library()
     keys = _u32_tensor(keys, "keys")
     values = _u32_tensor(values, "values")
+    _same_device(values, "values", keys.device)
     n = keys.numel()
     if values.numel() != n:
-        raise ValueError("keys and values differ in length")
-    if keys_out is None:
-        keys_out = torch.empty_like(keys)
-    if values_out is None:
-        values_out = torch.empty_like(values)
-    if workspace is None:
-        workspace = _workspace(lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 1), keys.device)
+        _bad("keys and values differ in length")
+    keys_out = _output(keys_out, "keys_out", keys)
+    values_out = _output(values_out, "values_out", values)
+    workspace = _workspace(workspace, lib.radix_sort_workspace_size(n, begin_bit, end_bit, digit_bits, 1,
+                                                                    _opt(options)), keys.device)
     _check(lib.radix_sort_pairs(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, begin_bit,
-                                end_bit, digit_bits, _ptr(workspace), workspace.numel(), _stream(keys)),
-           "radix_sort_pairs")
+                                end_bit, digit_bits, _ptr(workspace), workspace.numel(), _stream(keys),
+                                _opt(options)), "radix_sort_pairs")
     return keys_out, values_out
 
 
@@ -188,31 +337,32 @@ _KEY_DTYPES = {torch.uint32: "u32", torch.int32: "i32", torch.float32: "f32",
 
 
 def _typed_keys(keys: torch.Tensor, key_type: str | None):
-    if not isinstance(keys, torch.Tensor) or not keys.is_cuda:
-        raise ValueError("keys must be a GPU tensor")
+    _gpu_input(keys, "keys")
     if keys.dtype not in _KEY_DTYPES:
-        raise ValueError(f"keys must be a 32- or 64-bit integer or float tensor, got {keys.dtype}")
-    if keys.dim() != 1 or not keys.is_contiguous():
-        raise ValueError("keys must be a contiguous 1-D tensor")
+        _bad(f"keys must be a 32- or 64-bit integer or float tensor, got {keys.dtype}")
+    if keys.dim() != 1:
+        _bad("keys must be a 1-D tensor")
     kt = _KEY_DTYPES[keys.dtype] if key_type is None else key_type
     if kt not in _KEY_TYPES:
-        raise ValueError(f"key_type must be one of {sorted(_KEY_TYPES)}")
+        _bad(f"key_type must be one of {sorted(_KEY_TYPES)}")
     if (kt.endswith("64")) != (keys.element_size() == 8):
-        raise ValueError(f"key_type {kt} does not match a {keys.element_size() * 8}-bit tensor")
+        _bad(f"key_type {kt} does not match a {keys.element_size() * 8}-bit tensor")
     return _KEY_TYPES[kt]
 
 
 def radix_sort_typed_workspace_size(n: int, key_type: str, begin_bit: int = 0, end_bit: int | None = None,
-                                    digit_bits: int = 8, with_values: bool = False) -> int:
+                                    digit_bits: int = 8, with_values: bool = False,
+                                    options: SortOptions | None = None) -> int:
     if end_bit is None:
         end_bit = 64 if key_type.endswith("64") else 32
     return int(load_library().radix_sort_typed_workspace_size(n, _KEY_TYPES[key_type], begin_bit, end_bit,
-                                                              digit_bits, int(with_values)))
+                                                              digit_bits, int(with_values), _opt(options)))
 
 
 def radix_sort_keys_typed(keys: torch.Tensor, descending: bool = False, key_type: str | None = None,
                           begin_bit: int = 0, end_bit: int | None = None, digit_bits: int = 8,
-                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          options: SortOptions | None = None) -> torch.Tensor:
     """Stable sort of 32- or 64-bit keys as unsigned, signed or float (from the dtype
     unless key_type is given); end_bit defaults to the key width."""
     lib = load_library()
@@ -220,13 +370,11 @@ def radix_sort_keys_typed(keys: torch.Tensor, descending: bool = False, key_type
     if end_bit is None:
         end_bit = 8 * keys.element_size()
     n = keys.numel()
-    if out is None:
-        out = torch.empty_like(keys)
-    if workspace is None:
-        workspace = _workspace(lib.radix_sort_typed_workspace_size(n, kt, begin_bit, end_bit, digit_bits, 0),
-                               keys.device)
+    out = _output(out, "out", keys)
+    workspace = _workspace(workspace, lib.radix_sort_typed_workspace_size(n, kt, begin_bit, end_bit, digit_bits, 0,
+                                                                          _opt(options)), keys.device)
     _check(lib.radix_sort_keys_typed(_ptr(keys), _ptr(out), n, kt, int(descending), begin_bit, end_bit,
-                                     digit_bits, _ptr(workspace), workspace.numel(), _stream(keys)),
+                                     digit_bits, _ptr(workspace), workspace.numel(), _stream(keys), _opt(options)),
            "radix_sort_keys_typed")
     return out
 
@@ -234,86 +382,78 @@ def radix_sort_keys_typed(keys: torch.Tensor, descending: bool = False, key_type
 def radix_sort_pairs_typed(keys: torch.Tensor, values: torch.Tensor, descending: bool = False,
                            key_type: str | None = None, begin_bit: int = 0, end_bit: int | None = None,
                            digit_bits: int = 8, keys_out: torch.Tensor | None = None,
-                           values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                           values_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           options: SortOptions | None = None):
     """As radix_sort_keys_typed, carrying one 32-bit payload per key; returns (keys, values)."""
     lib = load_library()
     kt = _typed_keys(keys, key_type)
     if end_bit is None:
         end_bit = 8 * keys.element_size()
     values = _u32_tensor(values, "values")
+    _same_device(values, "values", keys.device)
     n = keys.numel()
     if values.numel() != n:
-        raise ValueError("keys and values differ in length")
-    if keys_out is None:
-        keys_out = torch.empty_like(keys)
-    if values_out is None:
-        values_out = torch.empty_like(values)
-    if workspace is None:
-        workspace = _workspace(lib.radix_sort_typed_workspace_size(n, kt, begin_bit, end_bit, digit_bits, 1),
-                               keys.device)
+        _bad("keys and values differ in length")
+    keys_out = _output(keys_out, "keys_out", keys)
+    values_out = _output(values_out, "values_out", values)
+    workspace = _workspace(workspace, lib.radix_sort_typed_workspace_size(n, kt, begin_bit, end_bit, digit_bits, 1,
+                                                                          _opt(options)), keys.device)
     _check(lib.radix_sort_pairs_typed(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, kt,
                                       int(descending), begin_bit, end_bit, digit_bits, _ptr(workspace),
-                                      workspace.numel(), _stream(keys)), "radix_sort_pairs_typed")
+                                      workspace.numel(), _stream(keys), _opt(options)), "radix_sort_pairs_typed")
     return keys_out, values_out
 
 
-def segmented_row_sort(x: torch.Tensor, descending: bool = False, digit_bits: int = 8,
-                       values_out: torch.Tensor | None = None, indices_out: torch.Tensor | None = None,
-                       workspace: torch.Tensor | None = None):
-    """Sort every row of a 2-D fp16/bf16 GPU tensor; returns (values, int64 column indices)."""
-    lib = load_library()
-    if not isinstance(x, torch.Tensor) or not x.is_cuda:
-        raise ValueError("x must be a GPU tensor")
+def _rows_input(x):
+    _gpu_input(x, "x")
     if x.dtype == torch.float16:
         dtype = LRS_DTYPE_FP16
     elif x.dtype == torch.bfloat16:
         dtype = LRS_DTYPE_BF16
     else:
-        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
+        _bad(f"x must be float16 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        _bad("x must be a 2-D tensor")
+    return dtype
+
+
+def segmented_row_sort(x: torch.Tensor, descending: bool = False, digit_bits: int = 8,
+                       values_out: torch.Tensor | None = None, indices_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, options: SortOptions | None = None):
+    """Sort every row of a 2-D fp16/bf16 GPU tensor; returns (values, int64 column indices)."""
+    lib = load_library()
+    dtype = _rows_input(x)
     rows, n = x.shape
-    if values_out is None:
-        values_out = torch.empty_like(x)
-    if indices_out is None:
-        indices_out = torch.empty((rows, n), dtype=torch.int64, device=x.device)
-    if workspace is None:
-        workspace = _workspace(lib.segmented_row_sort_workspace_size(rows, n, digit_bits), x.device)
+    values_out = _output(values_out, "values_out", x)
+    indices_out = _output(indices_out, "indices_out", x, element_size=8, dtype=torch.int64)
+    workspace = _workspace(workspace, lib.segmented_row_sort_workspace_size(rows, n, digit_bits, _opt(options)),
+                           x.device)
     _check(lib.segmented_row_sort(_ptr(x), _ptr(values_out), _ptr(indices_out), rows, n, dtype,
                                   int(descending), digit_bits, _ptr(workspace), workspace.numel(),
-                                  _stream(x)), "segmented_row_sort")
+                                  _stream(x), _opt(options)), "segmented_row_sort")
     return values_out, indices_out
 
 
 def segmented_row_sort_pairs(x: torch.Tensor, payload: torch.Tensor, descending: bool = False,
                              digit_bits: int = 8, values_out: torch.Tensor | None = None,
-                             payload_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                             payload_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             options: SortOptions | None = None):
     """Sort every row of a 2-D fp16/bf16 GPU tensor carrying a same-shape 32-bit payload;
     returns (values, payload)."""
     lib = load_library()
-    if not isinstance(x, torch.Tensor) or not x.is_cuda:
-        raise ValueError("x must be a GPU tensor")
-    if x.dtype == torch.float16:
-        dtype = LRS_DTYPE_FP16
-    elif x.dtype == torch.bfloat16:
-        dtype = LRS_DTYPE_BF16
-    else:
-        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
-    if (not isinstance(payload, torch.Tensor) or not payload.is_cuda or payload.shape != x.shape
-            or payload.element_size() != 4 or not payload.is_contiguous()):
-        raise ValueError("payload must be a contiguous 32-bit GPU tensor of x's shape")
+    dtype = _rows_input(x)
+    _gpu_input(payload, "payload")
+    _same_device(payload, "payload", x.device)
+    if payload.shape != x.shape or payload.element_size() != 4:
+        _bad("payload must be a 32-bit tensor of x's shape")
     rows, n = x.shape
-    if values_out is None:
-        values_out = torch.empty_like(x)
-    if payload_out is None:
-        payload_out = torch.empty_like(payload)
-    if workspace is None:
-        workspace = _workspace(lib.segmented_row_sort_workspace_size(rows, n, digit_bits), x.device)
+    values_out = _output(values_out, "values_out", x)
+    payload_out = _output(payload_out, "payload_out", payload)
+    workspace = _workspace(workspace, lib.segmented_row_sort_workspace_size(rows, n, digit_bits, _opt(options)),
+                           x.device)
     _check(lib.segmented_row_sort_pairs(_ptr(x), _ptr(payload), _ptr(values_out), _ptr(payload_out), rows, n,
                                         dtype, int(descending), digit_bits, _ptr(workspace), workspace.numel(),
-                                        _stream(x)), "segmented_row_sort_pairs")
+                                        _stream(x), _opt(options)), "segmented_row_sort_pairs")
     return values_out, payload_out
 
 
@@ -325,54 +465,16 @@ def radix_sort_digit_histograms(keys: torch.Tensor, begin_bit: int = 0, end_bit:
     passes = -(-(end_bit - begin_bit) // digit_bits) if end_bit > begin_bit else 0
     hist = torch.empty((max(passes, 1), 1 << digit_bits), dtype=torch.int32, device=keys.device)
     _check(lib.radix_sort_digit_histograms(_ptr(keys), keys.numel(), begin_bit, end_bit, digit_bits,
-                                           _ptr(hist), _stream(keys)), "radix_sort_digit_histograms")
+                                           _ptr(hist), _stream(keys), None), "radix_sort_digit_histograms")
     return hist
 
 
-def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
+def copy_probe(src: torch.Tensor, dst: torch.Tensor, options: SortOptions | None = None) -> None:
+    """The bandwidth yardstick: copy src's bytes into dst with the library's streaming copy kernel."""
     lib = load_library()
+    _gpu_input(src, "src")
+    _same_device(dst, "dst", src.device)
     nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < nbytes:
-        raise ValueError("dst smaller than src")
-    _check(lib.radix_sort_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src)), "copy_probe")
-
-
-def radix_sort_set_scan_strategy(strategy: str) -> str:
-    """How single-row sorts find each tile's output offsets: "lookback" (default)
-    or "reduce-then-scan".  Returns the previous strategy."""
-    if strategy not in _SCAN_STRATEGIES:
-        raise ValueError(f"strategy must be one of {sorted(_SCAN_STRATEGIES)}")
-    old = load_library().radix_sort_set_scan_strategy(_SCAN_STRATEGIES[strategy])
-    return {v: k for k, v in _SCAN_STRATEGIES.items()}[old]
-
-
-def radix_sort_set_spin_limit(polls: int) -> int:
-    """Bound, in polls, on a sweep tile's wait for an earlier tile's counts.
-
-    Past it the tile counts its prefix from the keys (same result); 0 makes
-    every tile do so.  Returns the previous bound.
-    """
-    if not 0 <= polls <= 0xFFFFFFFF:
-        raise ValueError("polls must fit in 32 bits")
-    return int(load_library().radix_sort_set_spin_limit(polls))
-
-
-class KernelTimer:
-    """Context manager: HIP-event times of every kernel the library enqueues inside it.
-
-    After exit, ``ms`` and ``launches`` hold per-kind sums for the kinds
-    "clear", "histogram", "sweep", "copy", "resident".
-    """
-    KINDS = ("clear", "histogram", "sweep", "copy", "resident")
-
-    def __enter__(self):
-        _check(load_library().radix_sort_timing_begin(), "timing_begin")
-        return self
-
-    def __exit__(self, *exc):
-        ms = (ctypes.c_double * 5)()
-        nl = (ctypes.c_int * 5)()
-        _check(load_library().radix_sort_timing_end(ms, nl), "timing_end")
-        self.ms = dict(zip(self.KINDS, list(ms)))
-        self.launches = dict(zip(self.KINDS, list(nl)))
-        return False
+    if not dst.is_contiguous() or dst.numel() * dst.element_size() < nbytes:
+        _bad("dst must be contiguous and at least as large as src")
+    _check(lib.radix_sort_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src), _opt(options)), "copy_probe")

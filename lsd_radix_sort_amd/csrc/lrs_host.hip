@@ -19,6 +19,13 @@
 #include "../../include/lsd_radix_sort.h"
 #include "lrs_launch.h"
 
+// A caller's kernel timer: start/stop event pairs and the kind of each launch.
+struct lrs_timer {
+    std::vector<hipEvent_t> pool;  // pairs: start, stop
+    std::vector<int> kind;
+    size_t used = 0;
+};
+
 namespace lrs {
 
 // --------------------------------------------------- utility kernels
@@ -102,52 +109,45 @@ inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 bool digit_bits_ok(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
 
-// ---------------------------------------------------------------- timing
+// ------------------------------------------------------------ per call
 
-struct Timing {
-    bool on = false;
-    std::vector<hipEvent_t> pool;  // pairs: start, stop
-    std::vector<int> kind;
-    size_t used = 0;
-};
-Timing g_timing;
 constexpr size_t kMaxTimed = 65536;
-
-// Brackets one launch with events when timing is on.  Returns the pair index or -1.
-struct TimedLaunch {
-    int idx = -1;
-    hipStream_t s;
-    TimedLaunch(int kind, hipStream_t stream) : s(stream) {
-        if (!g_timing.on || g_timing.used >= kMaxTimed) return;
-        const size_t i = g_timing.used;
-        if (g_timing.pool.size() < 2 * (i + 1)) {
-            hipEvent_t a, b;
-            if (hipEventCreate(&a) != hipSuccess) return;
-            if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
-            g_timing.pool.push_back(a);
-            g_timing.pool.push_back(b);
-        }
-        if (hipEventRecord(g_timing.pool[2 * i], s) != hipSuccess) return;
-        g_timing.kind.resize(i + 1);
-        g_timing.kind[i] = kind;
-        g_timing.used = i + 1;
-        idx = static_cast<int>(i);
-    }
-    void done() {
-        if (idx >= 0) (void)hipEventRecord(g_timing.pool[2 * idx + 1], s);
-    }
-};
 
 // Polls of an unpublished look-back word before a tile counts its prefix from
 // the keys (about 1 us each, so the default is tens of milliseconds: far beyond
 // any wait of a running sort, and only a guarantee against waiting forever).
-constexpr uint32_t kDefaultSpinLimit = 1u << 16;
-uint32_t g_spin_limit = kDefaultSpinLimit;
-
-// Scan strategy of single-row sorts (LRS_SCAN_*); segmented rows always use the look-back.
-int g_scan_strategy = LRS_SCAN_LOOKBACK;
+constexpr uint32_t kDefaultSpinLimit = LRS_DEFAULT_SPIN_LIMIT;
 // Partitions of the reduce-then-scan path: two workgroups per CU.
 constexpr uint64_t kPartitions = 512;
+
+// Everything one call needs besides its arguments: the stream and the
+// caller's options.  Nothing is kept between calls.
+struct Ctx {
+    hipStream_t s = nullptr;
+    lrs_timer *timer = nullptr;
+    uint32_t spin_limit = kDefaultSpinLimit;  // 0: every tile counts its prefix from the keys
+    int scan = LRS_SCAN_LOOKBACK;
+    uint64_t wide_from = 0;
+};
+
+// False for an invalid option.
+bool make_ctx(void *stream, const lrs_options *o, Ctx &c) {
+    c.s = static_cast<hipStream_t>(stream);
+    if (o == nullptr) return true;
+    if (o->scan_strategy != LRS_SCAN_LOOKBACK && o->scan_strategy != LRS_SCAN_REDUCE_THEN_SCAN) return false;
+    c.scan = o->scan_strategy;
+    c.timer = o->timer;
+    if (o->spin_limit != 0) c.spin_limit = o->spin_limit;
+    if (o->prefix_from_keys) c.spin_limit = 0;
+    c.wide_from = o->wide_from;
+    return true;
+}
+
+uint64_t wide_from_of(const lrs_options *o) { return o ? o->wide_from : 0; }
+bool options_ok(const lrs_options *o) {
+    Ctx c;
+    return make_ctx(nullptr, o, c);
+}
 
 // ------------------------------------------------------------ planning
 
@@ -174,7 +174,10 @@ struct Plan {
 
 // kind: 0 keys, 1 pairs, 2 segmented
 // kind: 0 keys, 1 pairs, 2 segmented; key_bytes: 4 or 8 (segmented keys are 2 bytes)
-Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int b, int kind, int key_bytes = 4) {
+// wide_from: nonzero sends rows of at least that many elements (sorted by
+// sweeps) to the wide sweep as well.
+Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int b, int kind, int key_bytes = 4,
+               uint64_t wide_from = 0) {
     Plan p;
     const bool key64 = key_bytes == 8;
     p.rows = rows;
@@ -184,9 +187,6 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.end_bit = end_bit;
     p.passes = static_cast<int>(cdiv(static_cast<uint64_t>(end_bit - begin_bit), b));
     const uint64_t R = 1ull << b;
-    p.tile_cfg = choose_tile_cfg(rows, row_len, key64);
-    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, tile_cfg_of(key64, p.tile_cfg).tile));
-    p.num_tiles = rows * p.tiles_per_row;
     // A row needs the wide sweep (64-bit look-back words, 64-bit store
     // addresses) once its byte offsets pass what a 32-bit buffer offset
     // reaches (2^32 bytes) or its counts pass the 30-bit count of a 32-bit
@@ -194,6 +194,12 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     // keys and for row sorts (int64 index out).
     const uint64_t widest = (kind == 2) ? 8 : static_cast<uint64_t>(key_bytes);
     p.wide_status = row_len * widest >= (1ull << 32) || row_len >= (1ull << 30);
+    const bool resident = row_len <= kResidentMax && !key64;
+    if (wide_from != 0 && row_len >= wide_from && !resident) p.wide_status = true;
+    // the wide sweep exists for the largest tile shape only
+    p.tile_cfg = p.wide_status ? 2 : choose_tile_cfg(rows, row_len, key64);
+    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, tile_cfg_of(key64, p.tile_cfg).tile));
+    p.num_tiles = rows * p.tiles_per_row;
 
     // histogram: about kHistTargetBlocks workgroups in all, at least
     // kHistMinChunk keys each
@@ -232,7 +238,7 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
         }
     }
     p.total = off;
-    if (row_len <= kResidentMax && !key64) {
+    if (resident) {
         p.resident = true;
         p.total = 0;
     }
@@ -249,34 +255,60 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 // ------------------------------------------------------------ launches
 
+// Brackets one launch with events when the call has a timer.
+struct TimedLaunch {
+    int idx = -1;
+    const Ctx &c;
+    TimedLaunch(int kind, const Ctx &ctx) : c(ctx) {
+        lrs_timer *t = c.timer;
+        if (t == nullptr || t->used >= kMaxTimed) return;
+        const size_t i = t->used;
+        if (t->pool.size() < 2 * (i + 1)) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess) return;
+            if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+            t->pool.push_back(a);
+            t->pool.push_back(b);
+        }
+        if (hipEventRecord(t->pool[2 * i], c.s) != hipSuccess) return;
+        t->kind.resize(i + 1);
+        t->kind[i] = kind;
+        t->used = i + 1;
+        idx = static_cast<int>(i);
+    }
+    void done() {
+        if (idx >= 0) (void)hipEventRecord(c.timer->pool[2 * idx + 1], c.s);
+    }
+};
+
 // Whole-row resident sort, timed as kind 4.
 template <int KK, int PK>
-hipError_t resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s) {
-    TimedLaunch t(4, s);
-    const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, s);
+hipError_t resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, const Ctx &c) {
+    TimedLaunch t(4, c);
+    const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, c.s);
     t.done();
     return e;
 }
 
-hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, hipStream_t s) {
-    ClearArgs c{};
-    c.p[0] = need_hist ? reinterpret_cast<uint32_t *>(ws + p.off_hist) : nullptr;
-    c.words[0] = p.hist_words;
-    c.p[1] = reinterpret_cast<uint32_t *>(ws + p.off_counters);
-    c.words[1] = p.counter_words;
-    c.p[2] = reinterpret_cast<uint32_t *>(ws + p.off_status[0]);
-    c.words[2] = p.status_bytes / 4;
-    const uint64_t words = std::max<uint64_t>(c.words[0] * need_hist, c.words[2]);
+hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, const Ctx &c) {
+    ClearArgs a{};
+    a.p[0] = need_hist ? reinterpret_cast<uint32_t *>(ws + p.off_hist) : nullptr;
+    a.words[0] = p.hist_words;
+    a.p[1] = reinterpret_cast<uint32_t *>(ws + p.off_counters);
+    a.words[1] = p.counter_words;
+    a.p[2] = reinterpret_cast<uint32_t *>(ws + p.off_status[0]);
+    a.words[2] = p.status_bytes / 4;
+    const uint64_t words = std::max<uint64_t>(a.words[0] * need_hist, a.words[2]);
     const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(2048, std::max<uint64_t>(1, cdiv(words / 4, kBlock))));
-    TimedLaunch t(0, s);
-    clear_kernel<<<blocks, kBlock, 0, s>>>(c);
+    TimedLaunch t(0, c);
+    clear_kernel<<<blocks, kBlock, 0, c.s>>>(a);
     hipError_t e = hipGetLastError();
     t.done();
     return e;
 }
 
 hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint64_t flip, uint64_t flip_neg,
-                            bool accumulate, hipStream_t s) {
+                            bool accumulate, const Ctx &c) {
     HistArgs h{};
     h.keys = keys;
     h.hist = hist;
@@ -288,18 +320,18 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     h.flip = flip;
     h.flip_neg = flip_neg;
     h.atomic = accumulate ? 1u : 0u;
-    const uint64_t blocks = p.rows * p.hist_chunks_per_row;
-    TimedLaunch t(1, s);
-    hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, static_cast<uint32_t>(blocks), s)
-                   : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, static_cast<uint32_t>(blocks), s)
-                   : (kk == kKeyU64) ? launch_hist<kKeyU64>(p.b, h, static_cast<uint32_t>(blocks), s)
-                   : (kk == kKeyX64) ? launch_hist<kKeyX64>(p.b, h, static_cast<uint32_t>(blocks), s)
-                                     : launch_hist<kKeyF16>(p.b, h, static_cast<uint32_t>(blocks), s);
+    const uint32_t blocks = static_cast<uint32_t>(p.rows * p.hist_chunks_per_row);
+    TimedLaunch t(1, c);
+    hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, blocks, c.s)
+                   : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, blocks, c.s)
+                   : (kk == kKeyU64) ? launch_hist<kKeyU64>(p.b, h, blocks, c.s)
+                   : (kk == kKeyX64) ? launch_hist<kKeyX64>(p.b, h, blocks, c.s)
+                                     : launch_hist<kKeyF16>(p.b, h, blocks, c.s);
     t.done();
     return e;
 }
 
-SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass) {
+SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass, const Ctx &c) {
     SweepArgs a{};
     const uint64_t R = 1ull << p.b;
     a.hist = reinterpret_cast<const uint32_t *>(ws + p.off_hist) + static_cast<uint64_t>(pass) * R;
@@ -316,7 +348,7 @@ SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass) {
     a.digit_mask = (1u << width) - 1u;
     a.flip = 0;
     a.flip_neg = 0;
-    a.spin_limit = g_spin_limit;
+    a.spin_limit = c.spin_limit;
     return a;
 }
 
@@ -357,7 +389,7 @@ bool key_type_is_64(int key_type) {
 // look-back; the upsweep reads the keys once more per pass.
 int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip_neg, bool pairs,
                              const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
-                             uint32_t *vals_out, uint8_t *ws, hipStream_t s) {
+                             uint32_t *vals_out, uint8_t *ws, const Ctx &c) {
     const uint64_t part_tiles = cdiv(p.num_tiles, std::min<uint64_t>(p.num_tiles, kPartitions));
     const uint64_t partitions = cdiv(p.num_tiles, part_tiles);
     uint32_t *counts = reinterpret_cast<uint32_t *>(ws + p.off_status[0]);  // partitions x R <= tiles x R
@@ -366,7 +398,7 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
     const uint32_t *src_k = keys_in;
     const uint32_t *src_v = vals_in;
     for (int pass = 0; pass < p.passes; ++pass) {
-        SweepArgs a = pass_args(p, ws, pass);
+        SweepArgs a = pass_args(p, ws, pass, c);
         PartArgs pa{};
         pa.keys = src_k;
         pa.counts = counts;
@@ -378,9 +410,9 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
         pa.flip = flip;
         pa.flip_neg = flip_neg;
         {
-            TimedLaunch t(1, s);
-            const hipError_t e = (kk == kKeyU32) ? launch_partition_counts<kKeyU32>(p.b, pa, s)
-                                                 : launch_partition_counts<kKeyX32>(p.b, pa, s);
+            TimedLaunch t(1, c);
+            const hipError_t e = (kk == kKeyU32) ? launch_partition_counts<kKeyU32>(p.b, pa, c.s)
+                                                 : launch_partition_counts<kKeyX32>(p.b, pa, c.s);
             t.done();
             if (e != hipSuccess) return LRS_ERR_HIP;
         }
@@ -392,17 +424,17 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
         a.part_offsets = counts;
         a.part_tiles = static_cast<uint32_t>(part_tiles);
         hipError_t e;
-        TimedLaunch t(2, s);
+        TimedLaunch t(2, c);
         if (pairs) {
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s)
-                                : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s)
+                                : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s)
-                                : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s)
+                                : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -415,12 +447,14 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
 // two-mask transform (KK = kKeyX32).
 int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t *keys_in,
             const uint32_t *vals_in, uint32_t *keys_out, uint32_t *vals_out, uint64_t n, int begin_bit,
-            int end_bit, int b, void *workspace, size_t ws_bytes, void *stream) {
+            int end_bit, int b, void *workspace, size_t ws_bytes, void *stream, const lrs_options *opts) {
+    Ctx c;
+    if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
     if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
     if (n == 0) return LRS_OK;
-    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0);
+    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0, 4, c.wide_from);
     if (!keys_in || !keys_out || (pairs && (!vals_in || !vals_out)) || (p.total && !workspace))
         return LRS_ERR_NULL_POINTER;
     if (misaligned(keys_in, 4) || misaligned(keys_out, 4) || misaligned(workspace, 256) ||
@@ -434,7 +468,6 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
                    overlaps(vals_out, kb, workspace, p.total))))
         return LRS_ERR_ALIASING;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.resident) {
         ResidentArgs r{};
         r.keys_in = keys_in;
@@ -448,17 +481,17 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
         r.flip_neg = flip_neg;
         hipError_t e;
         if (kk == kKeyU32)
-            e = pairs ? resident<kKeyU32, kResU32>(b, r, 1, n, s) : resident<kKeyU32, kResNone>(b, r, 1, n, s);
+            e = pairs ? resident<kKeyU32, kResU32>(b, r, 1, n, c) : resident<kKeyU32, kResNone>(b, r, 1, n, c);
         else
-            e = pairs ? resident<kKeyX32, kResU32>(b, r, 1, n, s) : resident<kKeyX32, kResNone>(b, r, 1, n, s);
+            e = pairs ? resident<kKeyX32, kResU32>(b, r, 1, n, c) : resident<kKeyX32, kResNone>(b, r, 1, n, c);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    if (g_scan_strategy == LRS_SCAN_REDUCE_THEN_SCAN)
-        return sort_32_reduce_then_scan(p, kk, flip, flip_neg, pairs, keys_in, vals_in, keys_out, vals_out, ws, s);
+    if (c.scan == LRS_SCAN_REDUCE_THEN_SCAN)
+        return sort_32_reduce_then_scan(p, kk, flip, flip_neg, pairs, keys_in, vals_in, keys_out, vals_out, ws, c);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, s) != hipSuccess)
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, c) != hipSuccess)
         return LRS_ERR_HIP;
 
     uint32_t *alt_k = reinterpret_cast<uint32_t *>(ws + p.off_alt_keys);
@@ -466,24 +499,24 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
     const uint32_t *src_k = keys_in;
     const uint32_t *src_v = vals_in;
     for (int pass = 0; pass < p.passes; ++pass) {
-        SweepArgs a = pass_args(p, ws, pass);
+        SweepArgs a = pass_args(p, ws, pass, c);
         uint32_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
         a.keys_in = src_k;
         a.keys_out = dk;
         a.flip = flip;
         a.flip_neg = flip_neg;
         hipError_t e;
-        TimedLaunch t(2, s);
+        TimedLaunch t(2, c);
         if (pairs) {
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
+                                : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
+                                : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -497,12 +530,14 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
 // resident sort and no reduce-then-scan.
 int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t *keys_in,
             const uint32_t *vals_in, uint64_t *keys_out, uint32_t *vals_out, uint64_t n, int begin_bit,
-            int end_bit, int b, void *workspace, size_t ws_bytes, void *stream) {
+            int end_bit, int b, void *workspace, size_t ws_bytes, void *stream, const lrs_options *opts) {
+    Ctx c;
+    if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
     if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 64 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
     if (n == 0) return LRS_OK;
-    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0, 8);
+    const Plan p = make_plan(1, n, begin_bit, end_bit, b, pairs ? 1 : 0, 8, c.wide_from);
     if (!keys_in || !keys_out || (pairs && (!vals_in || !vals_out)) || !workspace) return LRS_ERR_NULL_POINTER;
     if (misaligned(keys_in, 8) || misaligned(keys_out, 8) || misaligned(workspace, 256) ||
         (pairs && (misaligned(vals_in, 4) || misaligned(vals_out, 4))))
@@ -515,35 +550,133 @@ int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t
                    overlaps(vals_out, vb, workspace, p.total))))
         return LRS_ERR_ALIASING;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, s) != hipSuccess)
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, c) != hipSuccess)
         return LRS_ERR_HIP;
     uint64_t *alt_k = reinterpret_cast<uint64_t *>(ws + p.off_alt_keys);
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
     const uint64_t *src_k = keys_in;
     const uint32_t *src_v = vals_in;
     for (int pass = 0; pass < p.passes; ++pass) {
-        SweepArgs a = pass_args(p, ws, pass);
+        SweepArgs a = pass_args(p, ws, pass, c);
         uint64_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
         a.keys_in = src_k;
         a.keys_out = dk;
         a.flip = flip;
         a.flip_neg = flip_neg;
         hipError_t e;
-        TimedLaunch t(2, s);
+        TimedLaunch t(2, c);
         if (pairs) {
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
+                                : launch_sweep<kKeyX64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
             src_v = dv;
         } else {
-            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s)
-                                : launch_sweep<kKeyX64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
+                                : launch_sweep<kKeyX64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+        }
+        t.done();
+        if (e != hipSuccess) return LRS_ERR_HIP;
+        src_k = dk;
+    }
+    return LRS_OK;
+}
+
+// Shape checks shared by the two row sorts; LRS_OK or the status to return.
+int check_rows(int64_t rows, int64_t n, int dtype, int digit_bits) {
+    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
+    if (dtype != LRS_DTYPE_FP16 && dtype != LRS_DTYPE_BF16) return LRS_ERR_DTYPE;
+    if (rows < 0 || n < 0 || static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
+        (rows > 0 && static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40)))
+        return LRS_ERR_SIZE;
+    return LRS_OK;
+}
+
+// Row sorts: rows x n 16-bit patterns; payload either the column index made in
+// the kernels (pay_in == NULL, idx_out int64) or a caller's u32 per element.
+int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out, void *pay_out, int64_t rows,
+             int64_t n, int dtype, int descending, int digit_bits, void *workspace, size_t workspace_bytes,
+             void *stream, const lrs_options *opts) {
+    Ctx c;
+    if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
+    const int st = check_rows(rows, n, dtype, digit_bits);
+    if (st != LRS_OK) return st;
+    if (rows == 0 || n == 0) return LRS_OK;
+    const bool index = pay_in == nullptr;
+    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2, 4, c.wide_from);
+    if (!vals_in || !vals_out || !pay_out || (p.total && !workspace)) return LRS_ERR_NULL_POINTER;
+    const uint64_t pay_size = index ? 8 : 4;
+    if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(pay_out, pay_size) ||
+        (!index && misaligned(pay_in, 4)) || misaligned(workspace, 256))
+        return LRS_ERR_ALIGNMENT;
+    if (p.num_tiles > 0x7FFFFFFFull || p.rows * p.hist_chunks_per_row > 0x7FFFFFFFull) return LRS_ERR_SIZE;
+    if (p.resident && rows > 0x7FFFFFFF) return LRS_ERR_SIZE;
+    if (workspace_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
+    const uint64_t cnt = static_cast<uint64_t>(rows) * n;
+    const uint64_t vb = 2 * cnt, pb = pay_size * cnt, ib = 4 * cnt;
+    if (overlaps(vals_out, vb, vals_in, vb) || overlaps(pay_out, pb, vals_in, vb) ||
+        overlaps(pay_out, pb, vals_out, vb) || overlaps(vals_out, vb, workspace, p.total) ||
+        overlaps(pay_out, pb, workspace, p.total) ||
+        (!index && (overlaps(vals_out, vb, pay_in, ib) || overlaps(pay_out, pb, pay_in, ib))))
+        return LRS_ERR_ALIASING;
+
+    const uint32_t flip = descending ? 0xFFFFu : 0u;
+    if (p.resident) {
+        ResidentArgs r{};
+        r.keys_in = vals_in;
+        r.keys_out = vals_out;
+        r.vals_in = pay_in;
+        r.vals_out = pay_out;
+        r.row_len = static_cast<uint32_t>(n);
+        r.begin_bit = 0;
+        r.end_bit = 16;
+        r.flip = flip;
+        const hipError_t e = index ? resident<kKeyF16, kResIndex>(digit_bits, r, rows, n, c)
+                                   : resident<kKeyF16, kResU32>(digit_bits, r, rows, n, c);
+        return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    }
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
+    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
+    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, c) != hipSuccess)
+        return LRS_ERR_HIP;
+
+    uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
+    uint32_t *idx[2] = {reinterpret_cast<uint32_t *>(ws + p.off_idx[0]),
+                        reinterpret_cast<uint32_t *>(ws + p.off_idx[1])};
+    const uint16_t *src_k = vals_in;
+    const uint32_t *src_p = pay_in;
+    for (int pass = 0; pass < p.passes; ++pass) {
+        SweepArgs a = pass_args(p, ws, pass, c);
+        a.flip = flip;
+        uint16_t *dk = pass_dst(pass, p.passes, vals_out, alt_k);
+        a.keys_in = src_k;
+        a.keys_out = dk;
+        hipError_t e;
+        TimedLaunch t(2, c);
+        if (!index) {
+            // the caller's payload ping-pongs between pay_out and the first index buffer
+            uint32_t *dp = pass_dst(pass, p.passes, static_cast<uint32_t *>(pay_out), idx[0]);
+            a.vals_in = src_p;
+            a.vals_out = dp;
+            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            src_p = dp;
+        } else if (pass == 0) {
+            a.vals_in = nullptr;
+            a.vals_out = idx[0];
+            e = launch_sweep<kKeyF16, kPayIdxFirst, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+        } else if (pass + 1 < p.passes) {
+            a.vals_in = idx[(pass - 1) & 1];
+            a.vals_out = idx[pass & 1];
+            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+        } else {
+            a.vals_in = idx[(pass - 1) & 1];
+            a.vals_out = pay_out;
+            e = launch_sweep<kKeyF16, kPayIdxLast, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
         }
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
@@ -559,297 +692,167 @@ using namespace lrs;
 
 extern "C" {
 
-size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int digit_bits,
-                                 int with_values) {
-    if (!digit_bits_ok(digit_bits) || begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit ||
+size_t radix_sort_workspace_size(uint64_t n, int begin_bit, int end_bit, int digit_bits, int with_values,
+                                 const lrs_options *opts) {
+    if (!options_ok(opts) || !digit_bits_ok(digit_bits) || begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit ||
         n == 0 || n > LRS_MAX_KEYS)
         return 0;
-    return static_cast<size_t>(make_plan(1, n, begin_bit, end_bit, digit_bits, with_values ? 1 : 0).total);
+    return static_cast<size_t>(
+        make_plan(1, n, begin_bit, end_bit, digit_bits, with_values ? 1 : 0, 4, wide_from_of(opts)).total);
 }
 
-int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int begin_bit,
-                    int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
-                    void *stream) {
-    return sort_32(kKeyU32, 0, 0, false, keys_in, nullptr, keys_out, nullptr, n, begin_bit, end_bit,
-                   digit_bits, workspace, workspace_bytes, stream);
+int radix_sort_keys(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n, int begin_bit, int end_bit,
+                    int digit_bits, void *workspace, size_t workspace_bytes, void *stream, const lrs_options *opts) {
+    return sort_32(kKeyU32, 0, 0, false, keys_in, nullptr, keys_out, nullptr, n, begin_bit, end_bit, digit_bits,
+                   workspace, workspace_bytes, stream, opts);
 }
 
-int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
-                     uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
-                     void *workspace, size_t workspace_bytes, void *stream) {
-    return sort_32(kKeyU32, 0, 0, true, keys_in, vals_in, keys_out, vals_out, n, begin_bit, end_bit,
-                   digit_bits, workspace, workspace_bytes, stream);
+int radix_sort_pairs(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out, uint32_t *vals_out,
+                     uint64_t n, int begin_bit, int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
+                     void *stream, const lrs_options *opts) {
+    return sort_32(kKeyU32, 0, 0, true, keys_in, vals_in, keys_out, vals_out, n, begin_bit, end_bit, digit_bits,
+                   workspace, workspace_bytes, stream, opts);
 }
 
 size_t radix_sort_typed_workspace_size(uint64_t n, int key_type, int begin_bit, int end_bit, int digit_bits,
-                                       int with_values) {
+                                       int with_values, const lrs_options *opts) {
     int kk;
     uint64_t flip, flip_neg;
-    if (!key_transform(key_type, 0, kk, flip, flip_neg)) return 0;
+    if (!options_ok(opts) || !key_transform(key_type, 0, kk, flip, flip_neg)) return 0;
     const int key_bits = key_type_is_64(key_type) ? 64 : 32;
     if (!digit_bits_ok(digit_bits) || begin_bit < 0 || end_bit > key_bits || begin_bit >= end_bit || n == 0 ||
         n > LRS_MAX_KEYS)
         return 0;
-    return static_cast<size_t>(
-        make_plan(1, n, begin_bit, end_bit, digit_bits, with_values ? 1 : 0, key_bits / 8).total);
+    return static_cast<size_t>(make_plan(1, n, begin_bit, end_bit, digit_bits, with_values ? 1 : 0, key_bits / 8,
+                                         wide_from_of(opts)).total);
 }
 
 int radix_sort_keys_typed(const void *keys_in, void *keys_out, uint64_t n, int key_type, int descending,
-                          int begin_bit, int end_bit, int digit_bits, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+                          int begin_bit, int end_bit, int digit_bits, void *workspace, size_t workspace_bytes,
+                          void *stream, const lrs_options *opts) {
     int kk;
     uint64_t flip, flip_neg;
     if (!key_transform(key_type, descending, kk, flip, flip_neg)) return LRS_ERR_DTYPE;
     if (key_type_is_64(key_type))
         return sort_64(kk, flip, flip_neg, false, static_cast<const uint64_t *>(keys_in), nullptr,
                        static_cast<uint64_t *>(keys_out), nullptr, n, begin_bit, end_bit, digit_bits, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, opts);
     return sort_32(kk, flip, flip_neg, false, static_cast<const uint32_t *>(keys_in), nullptr,
                    static_cast<uint32_t *>(keys_out), nullptr, n, begin_bit, end_bit, digit_bits, workspace,
-                   workspace_bytes, stream);
+                   workspace_bytes, stream, opts);
 }
 
 int radix_sort_pairs_typed(const void *keys_in, const uint32_t *vals_in, void *keys_out, uint32_t *vals_out,
-                           uint64_t n, int key_type, int descending, int begin_bit, int end_bit,
-                           int digit_bits, void *workspace, size_t workspace_bytes, void *stream) {
+                           uint64_t n, int key_type, int descending, int begin_bit, int end_bit, int digit_bits,
+                           void *workspace, size_t workspace_bytes, void *stream, const lrs_options *opts) {
     int kk;
     uint64_t flip, flip_neg;
     if (!key_transform(key_type, descending, kk, flip, flip_neg)) return LRS_ERR_DTYPE;
     if (key_type_is_64(key_type))
         return sort_64(kk, flip, flip_neg, true, static_cast<const uint64_t *>(keys_in), vals_in,
                        static_cast<uint64_t *>(keys_out), vals_out, n, begin_bit, end_bit, digit_bits, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, opts);
     return sort_32(kk, flip, flip_neg, true, static_cast<const uint32_t *>(keys_in), vals_in,
                    static_cast<uint32_t *>(keys_out), vals_out, n, begin_bit, end_bit, digit_bits, workspace,
-                   workspace_bytes, stream);
+                   workspace_bytes, stream, opts);
 }
 
-size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits) {
-    if (!digit_bits_ok(digit_bits) || rows <= 0 || n <= 0 ||
-        static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
-        static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40))
+size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits, const lrs_options *opts) {
+    if (!options_ok(opts) || check_rows(rows, n, LRS_DTYPE_FP16, digit_bits) != LRS_OK || rows == 0 || n == 0)
         return 0;
-    return static_cast<size_t>(make_plan(rows, n, 0, 16, digit_bits, 2).total);
+    return static_cast<size_t>(make_plan(rows, n, 0, 16, digit_bits, 2, 4, wide_from_of(opts)).total);
 }
 
-int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx_out,
-                       int64_t rows, int64_t n, int dtype, int descending, int digit_bits,
-                       void *workspace, size_t workspace_bytes, void *stream) {
-    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
-    if (dtype != LRS_DTYPE_FP16 && dtype != LRS_DTYPE_BF16) return LRS_ERR_DTYPE;
-    if (rows < 0 || n < 0 || static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
-        (rows > 0 && static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40)))
-        return LRS_ERR_SIZE;
-    if (rows == 0 || n == 0) return LRS_OK;
-    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2);
-    if (!vals_in || !vals_out || !idx_out || (p.total && !workspace)) return LRS_ERR_NULL_POINTER;
-    if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(idx_out, 8) ||
-        misaligned(workspace, 256))
-        return LRS_ERR_ALIGNMENT;
-    if (p.num_tiles > 0x7FFFFFFFull || p.rows * p.hist_chunks_per_row > 0x7FFFFFFFull) return LRS_ERR_SIZE;
-    if (workspace_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
-    const uint64_t cnt = static_cast<uint64_t>(rows) * n;
-    if (overlaps(vals_out, 2 * cnt, vals_in, 2 * cnt) || overlaps(idx_out, 8 * cnt, vals_in, 2 * cnt) ||
-        overlaps(idx_out, 8 * cnt, vals_out, 2 * cnt) || overlaps(vals_out, 2 * cnt, workspace, p.total) ||
-        overlaps(idx_out, 8 * cnt, workspace, p.total))
-        return LRS_ERR_ALIASING;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint32_t flip = descending ? 0xFFFFu : 0u;
-    if (p.resident) {
-        if (rows > 0x7FFFFFFF) return LRS_ERR_SIZE;
-        ResidentArgs r{};
-        r.keys_in = vals_in;
-        r.keys_out = vals_out;
-        r.vals_out = idx_out;
-        r.row_len = static_cast<uint32_t>(n);
-        r.begin_bit = 0;
-        r.end_bit = 16;
-        r.flip = flip;
-        const hipError_t e = resident<kKeyF16, kResIndex>(digit_bits, r, rows, n, s);
-        return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
-    }
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-
-    uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
-    uint32_t *idx[2] = {reinterpret_cast<uint32_t *>(ws + p.off_idx[0]),
-                        reinterpret_cast<uint32_t *>(ws + p.off_idx[1])};
-    const uint16_t *src_k = vals_in;
-    for (int pass = 0; pass < p.passes; ++pass) {
-        SweepArgs a = pass_args(p, ws, pass);
-        a.flip = flip;
-        uint16_t *dk = pass_dst(pass, p.passes, vals_out, alt_k);
-        a.keys_in = src_k;
-        a.keys_out = dk;
-        hipError_t e;
-        TimedLaunch t(2, s);
-        if (pass == 0) {
-            a.vals_in = nullptr;
-            a.vals_out = idx[0];
-            e = launch_sweep<kKeyF16, kPayIdxFirst, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
-        } else if (pass + 1 < p.passes) {
-            a.vals_in = idx[(pass - 1) & 1];
-            a.vals_out = idx[pass & 1];
-            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
-        } else {
-            a.vals_in = idx[(pass - 1) & 1];
-            a.vals_out = idx_out;
-            e = launch_sweep<kKeyF16, kPayIdxLast, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
-        }
-        t.done();
-        if (e != hipSuccess) return LRS_ERR_HIP;
-        src_k = dk;
-    }
-    return LRS_OK;
+int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx_out, int64_t rows, int64_t n,
+                       int dtype, int descending, int digit_bits, void *workspace, size_t workspace_bytes,
+                       void *stream, const lrs_options *opts) {
+    return row_sort(vals_in, nullptr, vals_out, idx_out, rows, n, dtype, descending, digit_bits, workspace,
+                    workspace_bytes, stream, opts);
 }
 
 int segmented_row_sort_pairs(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out,
                              uint32_t *pay_out, int64_t rows, int64_t n, int dtype, int descending,
-                             int digit_bits, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
-    if (dtype != LRS_DTYPE_FP16 && dtype != LRS_DTYPE_BF16) return LRS_ERR_DTYPE;
-    if (rows < 0 || n < 0 || static_cast<uint64_t>(n) > LRS_MAX_ROW_LEN ||
-        (rows > 0 && static_cast<uint64_t>(rows) * static_cast<uint64_t>(n) >= (1ull << 40)))
-        return LRS_ERR_SIZE;
-    if (rows == 0 || n == 0) return LRS_OK;
-    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2);
-    if (!vals_in || !vals_out || !pay_in || !pay_out || (p.total && !workspace)) return LRS_ERR_NULL_POINTER;
-    if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(pay_in, 4) || misaligned(pay_out, 4) ||
-        misaligned(workspace, 256))
-        return LRS_ERR_ALIGNMENT;
-    if (p.num_tiles > 0x7FFFFFFFull || p.rows * p.hist_chunks_per_row > 0x7FFFFFFFull) return LRS_ERR_SIZE;
-    if (workspace_bytes < p.total) return LRS_ERR_WORKSPACE_TOO_SMALL;
-    const uint64_t cnt = static_cast<uint64_t>(rows) * n;
-    if (overlaps(vals_out, 2 * cnt, vals_in, 2 * cnt) || overlaps(vals_out, 2 * cnt, pay_in, 4 * cnt) ||
-        overlaps(pay_out, 4 * cnt, vals_in, 2 * cnt) || overlaps(pay_out, 4 * cnt, pay_in, 4 * cnt) ||
-        overlaps(pay_out, 4 * cnt, vals_out, 2 * cnt) || overlaps(vals_out, 2 * cnt, workspace, p.total) ||
-        overlaps(pay_out, 4 * cnt, workspace, p.total))
-        return LRS_ERR_ALIASING;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint32_t flip = descending ? 0xFFFFu : 0u;
-    if (p.resident) {
-        if (rows > 0x7FFFFFFF) return LRS_ERR_SIZE;
-        ResidentArgs r{};
-        r.keys_in = vals_in;
-        r.keys_out = vals_out;
-        r.vals_in = pay_in;
-        r.vals_out = pay_out;
-        r.row_len = static_cast<uint32_t>(n);
-        r.begin_bit = 0;
-        r.end_bit = 16;
-        r.flip = flip;
-        const hipError_t e = resident<kKeyF16, kResU32>(digit_bits, r, rows, n, s);
-        return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
-    }
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, s) != hipSuccess) return LRS_ERR_HIP;
-    uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
-    uint32_t *alt_p = reinterpret_cast<uint32_t *>(ws + p.off_idx[0]);
-    const uint16_t *src_k = vals_in;
-    const uint32_t *src_p = pay_in;
-    for (int pass = 0; pass < p.passes; ++pass) {
-        SweepArgs a = pass_args(p, ws, pass);
-        a.flip = flip;
-        uint16_t *dk = pass_dst(pass, p.passes, vals_out, alt_k);
-        uint32_t *dp = pass_dst(pass, p.passes, pay_out, alt_p);
-        a.keys_in = src_k;
-        a.keys_out = dk;
-        a.vals_in = src_p;
-        a.vals_out = dp;
-        TimedLaunch t(2, s);
-        const hipError_t e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, s);
-        t.done();
-        if (e != hipSuccess) return LRS_ERR_HIP;
-        src_k = dk;
-        src_p = dp;
-    }
-    return LRS_OK;
+                             int digit_bits, void *workspace, size_t workspace_bytes, void *stream,
+                             const lrs_options *opts) {
+    if (rows > 0 && n > 0 && pay_in == nullptr) return LRS_ERR_NULL_POINTER;
+    return row_sort(vals_in, pay_in, vals_out, pay_out, rows, n, dtype, descending, digit_bits, workspace,
+                    workspace_bytes, stream, opts);
 }
 
-int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit,
-                                int digit_bits, uint32_t *hist_out, void *stream) {
+int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit, int digit_bits,
+                                uint32_t *hist_out, void *stream, const lrs_options *opts) {
+    Ctx c;
+    if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
     if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
     if (!hist_out || (n && !keys)) return LRS_ERR_NULL_POINTER;
     if (misaligned(keys, 4) || misaligned(hist_out, 16)) return LRS_ERR_ALIGNMENT;
     const Plan p = make_plan(1, n ? n : 1, begin_bit, end_bit, digit_bits, 0);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    ClearArgs c{};
-    c.p[0] = hist_out;
-    c.words[0] = p.hist_words;
+    ClearArgs a{};
+    a.p[0] = hist_out;
+    a.words[0] = p.hist_words;
     {
-        TimedLaunch t(0, s);
-        clear_kernel<<<1, kBlock, 0, s>>>(c);
+        TimedLaunch t(0, c);
+        clear_kernel<<<1, kBlock, 0, c.s>>>(a);
         hipError_t e = hipGetLastError();
         t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
     }
     if (n == 0) return LRS_OK;
-    return launch_histogram(p, keys, hist_out, kKeyU32, 0, 0, true, s) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    return launch_histogram(p, keys, hist_out, kKeyU32, 0, 0, true, c) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
-int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream) {
+int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream, const lrs_options *opts) {
+    Ctx c;
+    if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
     if (bytes == 0) return LRS_OK;
     if (!src || !dst) return LRS_ERR_NULL_POINTER;
     if (misaligned(src, 16) || misaligned(dst, 16)) return LRS_ERR_ALIGNMENT;
     if (overlaps(src, bytes, dst, bytes)) return LRS_ERR_ALIASING;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const uint64_t n16 = bytes / 16;
     const uint32_t tail = static_cast<uint32_t>(bytes % 16);
     const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(1u << 20, std::max<uint64_t>(1, cdiv(n16, kBlock))));
-    TimedLaunch t(3, s);
-    copy_kernel<<<blocks, kBlock, 0, s>>>(static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16,
-                                          static_cast<const uint8_t *>(src) + n16 * 16,
-                                          static_cast<uint8_t *>(dst) + n16 * 16, tail);
+    TimedLaunch t(3, c);
+    copy_kernel<<<blocks, kBlock, 0, c.s>>>(static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16,
+                                            static_cast<const uint8_t *>(src) + n16 * 16,
+                                            static_cast<uint8_t *>(dst) + n16 * 16, tail);
     hipError_t e = hipGetLastError();
     t.done();
     return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
-int radix_sort_set_scan_strategy(int strategy) {
-    if (strategy != LRS_SCAN_LOOKBACK && strategy != LRS_SCAN_REDUCE_THEN_SCAN) return -1;
-    const int old = g_scan_strategy;
-    g_scan_strategy = strategy;
-    return old;
+lrs_timer *radix_sort_timer_create(void) {
+    try {
+        return new lrs_timer();
+    } catch (...) {
+        return nullptr;
+    }
 }
 
-uint32_t radix_sort_set_spin_limit(uint32_t polls) {
-    const uint32_t old = g_spin_limit;
-    g_spin_limit = polls;
-    return old;
-}
-
-int radix_sort_timing_begin(void) {
-    g_timing.on = true;
-    g_timing.used = 0;
-    g_timing.kind.clear();
-    return LRS_OK;
-}
-
-int radix_sort_timing_end(double *ms_by_kind, int *launches_by_kind) {
+int radix_sort_timer_read(lrs_timer *timer, double *ms_by_kind, int *launches_by_kind) {
     for (int k = 0; k < 5; ++k) {
         if (ms_by_kind) ms_by_kind[k] = 0.0;
         if (launches_by_kind) launches_by_kind[k] = 0;
     }
-    g_timing.on = false;
-    for (size_t i = 0; i < g_timing.used; ++i) {
-        if (hipEventSynchronize(g_timing.pool[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
+    if (timer == nullptr) return LRS_ERR_NULL_POINTER;
+    const size_t used = timer->used;
+    timer->used = 0;
+    for (size_t i = 0; i < used; ++i) {
+        if (hipEventSynchronize(timer->pool[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
         float ms = 0.f;
-        if (hipEventElapsedTime(&ms, g_timing.pool[2 * i], g_timing.pool[2 * i + 1]) != hipSuccess)
-            return LRS_ERR_HIP;
-        const int k = g_timing.kind[i];
+        if (hipEventElapsedTime(&ms, timer->pool[2 * i], timer->pool[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
+        const int k = timer->kind[i];
         if (ms_by_kind) ms_by_kind[k] += ms;
         if (launches_by_kind) launches_by_kind[k] += 1;
     }
-    g_timing.used = 0;
     return LRS_OK;
+}
+
+void radix_sort_timer_destroy(lrs_timer *timer) {
+    if (timer == nullptr) return;
+    for (hipEvent_t e : timer->pool) (void)hipEventDestroy(e);
+    delete timer;
 }
 
 const char *radix_sort_status_string(int status) {
@@ -864,6 +867,7 @@ const char *radix_sort_status_string(int status) {
         case LRS_ERR_DTYPE: return "dtype must be LRS_DTYPE_FP16 or LRS_DTYPE_BF16";
         case LRS_ERR_HIP: return "the HIP runtime rejected a launch";
         case LRS_ERR_ALIGNMENT: return "a pointer is not aligned as required";
+        case LRS_ERR_OPTION: return "an lrs_options field has an invalid value";
         default: return "unknown status";
     }
 }

@@ -22,6 +22,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lrs_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblrs_oracle.so")
+_CTX_SRC = os.path.join(_HERE, "std_sort_context.cpp")
+_CTX_PATH = os.path.join(_HERE, "libstd_sort_context.so")
 _lib = None
 
 OK = 0
@@ -35,7 +37,25 @@ def build(force: bool = True) -> str:
             ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, _SRC]
         )
         os.replace(tmp, _LIB_PATH)
+    if force or not os.path.exists(_CTX_PATH):
+        tmp = _CTX_PATH + ".tmp"
+        subprocess.check_call(["g++", "-std=c++17", "-O2", "-Wall", "-fPIC", "-shared", "-o", tmp, _CTX_SRC])
+        os.replace(tmp, _CTX_PATH)
     return _LIB_PATH
+
+
+def std_sort_seconds(keys: np.ndarray) -> float:
+    """Seconds std::sort takes on one core to sort a copy of these u32 keys (a
+    context figure for the benchmark, not part of the oracle)."""
+    if not os.path.exists(_CTX_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_CTX_PATH)
+    lib.std_sort_u32_seconds.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+    lib.std_sort_u32_seconds.restype = ctypes.c_double
+    a = np.ascontiguousarray(keys, dtype=np.uint32).copy()
+    secs = lib.std_sort_u32_seconds(a.ctypes.data, a.size)
+    assert np.all(a[1:] >= a[:-1]), "std::sort did not sort"
+    return float(secs)
 
 
 def _load():

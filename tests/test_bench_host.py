@@ -47,7 +47,20 @@ def test_workload_table_is_complete():
     for name, w in bench.WORKLOADS.items():
         assert w["kind"] in ("keys", "pairs", "rows") and w["b"] in (1, 2, 4, 8), name
         assert w["desc"], name
-    assert set(bench.MEASURED_SWEEP_TRAFFIC) <= set(bench.WORKLOADS)
-    # the traffic on record is within a few percent of the headline's algorithmic bytes per launch
-    ratio = bench.MEASURED_SWEEP_TRAFFIC[bench.HEADLINE] / (16 * (1 << 28))
-    assert 1.0 <= ratio < 1.1
+    assert set(bench.MEASURED_TRAFFIC) <= set(bench.WORKLOADS)
+    for name, m in bench.MEASURED_TRAFFIC.items():
+        assert set(m) >= {"kernel_sha16", "bytes_per_launch", "source"}, name
+        assert len(m["kernel_sha16"]) == 16 and m["bytes_per_launch"] > 0, name
+
+
+def test_traffic_is_tied_to_the_kernel_sources(monkeypatch):
+    """A counter figure is reported only for the kernel sources it was taken
+    on; after any change to them the line says null until it is re-measured."""
+    sha = bench.kernel_sources_sha16()
+    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", {"x": {"kernel_sha16": sha, "bytes_per_launch": 123,
+                                                          "source": "test"}})
+    assert bench.measured_traffic("x") == 123
+    assert bench.measured_traffic("y") is None
+    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", {"x": {"kernel_sha16": "0" * 16, "bytes_per_launch": 123,
+                                                          "source": "test"}})
+    assert bench.measured_traffic("x") is None

@@ -114,7 +114,7 @@ def test_typed_rejects_unknown_key_type():
     ws = torch.empty(1, dtype=torch.uint8, device="cuda")
     lib = lrs.load_library()
     st = lib.radix_sort_keys_typed(k.data_ptr(), o.data_ptr(), 16, 7, 0, 0, 32, 8, ws.data_ptr(), 1,
-                                   torch.cuda.current_stream().cuda_stream)
+                                   torch.cuda.current_stream().cuda_stream, None)
     assert st == 7  # LRS_ERR_DTYPE
 
 
