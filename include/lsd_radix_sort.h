@@ -243,6 +243,27 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
 int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream, const lrs_options *opts);
 
 /*
+ * radix_sort_pairs for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace argument: its workspace is a device array of
+ * LRS_NO_ALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  It calls no hipMalloc, hipFree or other allocating routine.
+ * Sizes whose workspace (radix_sort_workspace_size(n, ..., 1, opts)) exceeds
+ * the array return LRS_ERR_SIZE: with 8-bit digits over 32 bits, about 8.2
+ * million pairs (rows of at most 8192 pairs need no workspace at all).  Every
+ * call on one GPU shares that GPU's array, so calls that may run at the same
+ * time on one GPU (two streams, two threads) race and corrupt each other's
+ * results: order them, or use radix_sort_pairs with workspaces of their own.
+ * The first call on each device looks up the array's device address
+ * (LRS_ERR_HIP if the runtime cannot give it).  Arguments, result and other
+ * errors are those of radix_sort_pairs.
+ */
+#define LRS_NO_ALLOC_SCRATCH_BYTES (64ull << 20)
+int radix_sort_pairs_no_alloc(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+                              uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits,
+                              void *stream, const lrs_options *opts);
+
+/*
  * Kernel timing for measurement (opts->timer).  radix_sort_timer_create
  * returns a new timer (NULL if host memory runs out); calls given it in their
  * options bracket each kernel they enqueue with HIP events on their stream.

@@ -99,6 +99,7 @@ def load_library():
         "radix_sort_typed_workspace_size": ([u64, c_int, c_int, c_int, c_int, c_int, O], szt),
         "radix_sort_keys_typed": ([P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P, O], c_int),
         "radix_sort_pairs_typed": ([P, P, P, P, u64, c_int, c_int, c_int, c_int, c_int, P, szt, P, O], c_int),
+        "radix_sort_pairs_no_alloc": ([P, P, P, P, u64, c_int, c_int, c_int, P, O], c_int),
         "radix_sort_timer_create": ([], P),
         "radix_sort_timer_read": ([P, P, P], c_int),
         "radix_sort_timer_destroy": ([P], None),
@@ -327,6 +328,30 @@ def radix_sort_pairs(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 
     _check(lib.radix_sort_pairs(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, begin_bit,
                                 end_bit, digit_bits, _ptr(workspace), workspace.numel(), _stream(keys),
                                 _opt(options)), "radix_sort_pairs")
+    return keys_out, values_out
+
+
+NO_ALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def radix_sort_pairs_no_alloc(keys: torch.Tensor, values: torch.Tensor, begin_bit: int = 0, end_bit: int = 32,
+                              digit_bits: int = 8, keys_out: torch.Tensor | None = None,
+                              values_out: torch.Tensor | None = None, options: SortOptions | None = None):
+    """radix_sort_pairs with the library's own per-GPU scratch as workspace (the
+    C entry point allocates nothing; outputs are allocated here only if not
+    given).  Calls that may overlap on one GPU race.  Returns (keys, values)."""
+    lib = load_library()
+    keys = _u32_tensor(keys, "keys")
+    values = _u32_tensor(values, "values")
+    _same_device(values, "values", keys.device)
+    n = keys.numel()
+    if values.numel() != n:
+        _bad("keys and values differ in length")
+    keys_out = _output(keys_out, "keys_out", keys)
+    values_out = _output(values_out, "values_out", values)
+    _check(lib.radix_sort_pairs_no_alloc(_ptr(keys), _ptr(values), _ptr(keys_out), _ptr(values_out), n, begin_bit,
+                                         end_bit, digit_bits, _stream(keys), _opt(options)),
+           "radix_sort_pairs_no_alloc")
     return keys_out, values_out
 
 

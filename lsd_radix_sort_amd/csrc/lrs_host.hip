@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/lsd_radix_sort.h"
@@ -64,6 +65,37 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const uint4 *src, uint4 *d
     if (blockIdx.x == 0 && threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 
+
+// ------------------------------------------- scratch of the no-alloc entry
+
+// Device memory that radix_sort_pairs_no_alloc uses as its workspace, so it
+// needs no allocation.  Every GPU the library runs on holds its own copy for
+// the life of the process.  Host code never uses the name itself (on the host
+// it stands for a host-side symbol, not a device address): it uses the device
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[LRS_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices];  // per device; set once, under the mutex
+
+// The current device's scratch address, looked up on the first call on each
+// device (with that device current); NULL if the runtime cannot give it.
+void *scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
 
 namespace {
 
@@ -820,6 +852,25 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
     hipError_t e = hipGetLastError();
     t.done();
     return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
+int radix_sort_pairs_no_alloc(const uint32_t *keys_in, const uint32_t *vals_in, uint32_t *keys_out,
+                              uint32_t *vals_out, uint64_t n, int begin_bit, int end_bit, int digit_bits, void *stream,
+                              const lrs_options *opts) {
+    if (!options_ok(opts)) return LRS_ERR_OPTION;
+    if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
+    if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
+    if (n == 0) return LRS_OK;
+    if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
+    const uint64_t need = make_plan(1, n, begin_bit, end_bit, digit_bits, 1, 4, wide_from_of(opts)).total;
+    if (need > LRS_NO_ALLOC_SCRATCH_BYTES) return LRS_ERR_SIZE;
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = scratch_address();
+        if (ws == nullptr) return LRS_ERR_HIP;
+    }
+    return sort_32(kKeyU32, 0, 0, true, keys_in, vals_in, keys_out, vals_out, n, begin_bit, end_bit, digit_bits, ws,
+                   LRS_NO_ALLOC_SCRATCH_BYTES, stream, opts);
 }
 
 lrs_timer *radix_sort_timer_create(void) {
