@@ -198,7 +198,8 @@ struct Plan {
     uint32_t hist_chunks_per_row = 0;
     // workspace layout (byte offsets)
     uint64_t off_hist = 0, hist_words = 0;
-    uint64_t off_counters = 0, counter_words = 0;
+    uint64_t off_bases = 0;                      // hist_words bucket bases
+    uint64_t off_counters = 0, counter_words = 0;  // finished histogram workgroups, per row
     uint64_t off_status[2] = {0, 0}, status_bytes = 0;
     uint64_t off_alt_keys = 0, off_alt_vals = 0, off_idx[2] = {0, 0};
     uint64_t total = 0;
@@ -244,8 +245,10 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.off_hist = off;
     p.hist_words = rows * p.passes * R;
     off = align_up(off + 4 * p.hist_words, kAlign);
+    p.off_bases = off;
+    off = align_up(off + 4 * p.hist_words, kAlign);
     p.off_counters = off;
-    p.counter_words = static_cast<uint64_t>(p.passes) * kXcds;
+    p.counter_words = rows;
     off = align_up(off + 4 * p.counter_words, kAlign);
     p.status_bytes = p.num_tiles * R * (p.wide_status ? 8 : 4);
     const int status_bufs = p.passes > 1 ? 2 : 1;
@@ -339,11 +342,15 @@ hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, const Ctx &c
     return e;
 }
 
+// All passes' digit counts into `hist`; with `ws` also the bucket bases (the
+// row's last histogram workgroup scans them), for the sweeps.
 hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int kk, uint64_t flip, uint64_t flip_neg,
-                            bool accumulate, const Ctx &c) {
+                            bool accumulate, uint8_t *ws, const Ctx &c) {
     HistArgs h{};
     h.keys = keys;
     h.hist = hist;
+    h.bases = ws ? reinterpret_cast<uint32_t *>(ws + p.off_bases) : nullptr;
+    h.done = ws ? reinterpret_cast<uint32_t *>(ws + p.off_counters) : nullptr;
     h.row_len = static_cast<uint32_t>(p.row_len);
     h.chunks_per_row = p.hist_chunks_per_row;
     h.passes = static_cast<uint32_t>(p.passes);
@@ -366,11 +373,10 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
 SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass, const Ctx &c) {
     SweepArgs a{};
     const uint64_t R = 1ull << p.b;
-    a.hist = reinterpret_cast<const uint32_t *>(ws + p.off_hist) + static_cast<uint64_t>(pass) * R;
-    a.hist_row_stride = static_cast<uint32_t>(p.passes * R);
+    a.bases = reinterpret_cast<const uint32_t *>(ws + p.off_bases) + static_cast<uint64_t>(pass) * R;
+    a.bases_row_stride = static_cast<uint32_t>(p.passes * R);
     a.status = ws + p.off_status[pass & 1];
     a.status_next = (pass + 1 < p.passes) ? ws + p.off_status[(pass + 1) & 1] : nullptr;
-    a.tile_counter = reinterpret_cast<uint32_t *>(ws + p.off_counters) + static_cast<uint64_t>(pass) * kXcds;
     a.row_len = static_cast<uint32_t>(p.row_len);
     a.tiles_per_row = p.tiles_per_row;
     a.num_tiles = static_cast<uint32_t>(p.num_tiles);
@@ -523,7 +529,7 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
         return sort_32_reduce_then_scan(p, kk, flip, flip_neg, pairs, keys_in, vals_in, keys_out, vals_out, ws, c);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, c) != hipSuccess)
+    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, ws, c) != hipSuccess)
         return LRS_ERR_HIP;
 
     uint32_t *alt_k = reinterpret_cast<uint32_t *>(ws + p.off_alt_keys);
@@ -585,7 +591,7 @@ int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, c) != hipSuccess)
+    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, ws, c) != hipSuccess)
         return LRS_ERR_HIP;
     uint64_t *alt_k = reinterpret_cast<uint64_t *>(ws + p.off_alt_keys);
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
@@ -658,23 +664,24 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
 
     const uint32_t flip = descending ? 0xFFFFu : 0u;
     if (p.resident) {
-        ResidentArgs r{};
+        RowResidentArgs r{};
         r.keys_in = vals_in;
         r.keys_out = vals_out;
-        r.vals_in = pay_in;
-        r.vals_out = pay_out;
+        r.pay_in = pay_in;
+        r.pay_out = pay_out;
+        r.rows = static_cast<uint32_t>(rows);
         r.row_len = static_cast<uint32_t>(n);
-        r.begin_bit = 0;
-        r.end_bit = 16;
         r.flip = flip;
-        const hipError_t e = index ? resident<kKeyF16, kResIndex>(digit_bits, r, rows, n, c)
-                                   : resident<kKeyF16, kResU32>(digit_bits, r, rows, n, c);
+        TimedLaunch t(4, c);
+        const hipError_t e = index ? launch_row_resident<kResIndex>(digit_bits, r, c.s)
+                                   : launch_row_resident<kResU32>(digit_bits, r, c.s);
+        t.done();
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
     if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, c) != hipSuccess)
+    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, ws, c) != hipSuccess)
         return LRS_ERR_HIP;
 
     uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
@@ -832,7 +839,7 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
         if (e != hipSuccess) return LRS_ERR_HIP;
     }
     if (n == 0) return LRS_OK;
-    return launch_histogram(p, keys, hist_out, kKeyU32, 0, 0, true, c) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+    return launch_histogram(p, keys, hist_out, kKeyU32, 0, 0, true, nullptr, c) == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
 int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream, const lrs_options *opts) {

@@ -8,6 +8,6 @@ template hipError_t launch_sweep<kKeyF16, kPayIdxFirst, false>(int, const SweepA
 template hipError_t launch_sweep<kKeyF16, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
 template hipError_t launch_sweep<kKeyF16, kPayIdxLast, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
 template hipError_t launch_hist<kKeyF16>(int, const HistArgs &, uint32_t, hipStream_t);
-template hipError_t launch_resident<kKeyF16, kResIndex>(int, const ResidentArgs &, uint64_t, uint64_t, hipStream_t);
-template hipError_t launch_resident<kKeyF16, kResU32>(int, const ResidentArgs &, uint64_t, uint64_t, hipStream_t);
+template hipError_t launch_row_resident<kResIndex>(int, const RowResidentArgs &, hipStream_t);
+template hipError_t launch_row_resident<kResU32>(int, const RowResidentArgs &, hipStream_t);
 }  // namespace lrs

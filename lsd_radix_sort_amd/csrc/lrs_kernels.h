@@ -41,6 +41,10 @@ namespace lrs {
 #ifndef LRS_XCD_CHUNK
 #define LRS_XCD_CHUNK 16        // consecutive sweep tiles handed to one XCD at a time
 #endif
+#ifndef LRS_SWEEP_WAVES_PER_EU
+#define LRS_SWEEP_WAVES_PER_EU 4  // register budget of the sweep (4: 128 VGPRs)
+#endif
+
 
 constexpr int kBlock = 256;            // threads per workgroup (histogram, utilities)
 constexpr int kSweepBlock = LRS_SWEEP_BLOCK;
@@ -183,18 +187,18 @@ __device__ inline void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
 
 // --------------------------------------------------------- wave utilities
 
-// Lanes of this wave whose digit differs from this lane's digit (all 64 lanes
-// must be active).  For each of the digit's B bits the ballot gives the lanes
-// with the bit set; XOR with this lane's bit spread to all 32 bits (0 or ~0)
-// leaves the lanes that differ in that bit, and the mismatch mask is the OR of
-// those over all bits.  v_bitop3 does XOR and OR in one instruction: with
-// operands (spread, acc, ballot) the table 0xDE is acc | (spread ^ ballot).
+// Lanes of this wave whose digit equals this lane's digit (all 64 lanes must
+// be active).  For each of the digit's B bits the ballot gives the lanes with
+// the bit set; XNOR with this lane's bit spread to all 32 bits (0 or ~0) keeps
+// the lanes that agree in that bit, and the match mask is the AND of those
+// over all bits.  v_bitop3 does the XNOR and the AND in one instruction: with
+// operands (spread, acc, ballot) the table 0x84 is acc & ~(spread ^ ballot).
 // The ballots are taken from the spreads themselves (one compare each; the
 // pin stops the compiler from deriving them from d with a shift and a compare
 // instead), all before the accumulation, so each lands in its own scalar
 // register pair and no compare waits on the one before it.
 template <int B>
-__device__ inline uint64_t mismatch_mask(uint32_t d) {
+__device__ inline uint64_t match_mask(uint32_t d) {
     uint32_t spread[B];
     uint64_t bal[B];
 #pragma unroll
@@ -204,11 +208,11 @@ __device__ inline uint64_t mismatch_mask(uint32_t d) {
     }
 #pragma unroll
     for (int i = 0; i < B; ++i) bal[i] = __builtin_amdgcn_ballot_w64(spread[i] != 0u);
-    uint32_t lo = 0u, hi = 0u;
+    uint32_t lo = ~0u, hi = ~0u;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-        lo = __builtin_amdgcn_bitop3_b32(spread[i], lo, static_cast<uint32_t>(bal[i]), 0xDE);
-        hi = __builtin_amdgcn_bitop3_b32(spread[i], hi, static_cast<uint32_t>(bal[i] >> 32), 0xDE);
+        lo = __builtin_amdgcn_bitop3_b32(spread[i], lo, static_cast<uint32_t>(bal[i]), 0x84);
+        hi = __builtin_amdgcn_bitop3_b32(spread[i], hi, static_cast<uint32_t>(bal[i] >> 32), 0x84);
     }
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
@@ -219,19 +223,28 @@ __device__ inline uint32_t count_below(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
-// This lane's rank among the lanes of its digit group, and the group's size,
-// from the group's mismatch mask.
-__device__ inline void group_rank_from_mismatch(uint64_t mismatch, int lane, uint32_t &below, uint32_t &size) {
-    below = static_cast<uint32_t>(lane) - count_below(mismatch);
-    size = 64u - static_cast<uint32_t>(__popcll(mismatch));
+// This lane's rank among the lanes of its digit group (the group members at
+// lower lanes), and the group's size, from the group's member mask.
+__device__ inline void group_rank(uint64_t members, uint32_t &below, uint32_t &size) {
+    below = count_below(members);
+    size = static_cast<uint32_t>(__popcll(members));
 }
 
-__device__ inline uint32_t wave_inclusive_scan(uint32_t x, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+// Inclusive sum over the lanes of a wave (all 64 lanes active), by DPP lane
+// moves: shifts of 1, 2, 4 and 8 lanes within each row of 16 lanes, then lane
+// 15 of each row added to the next row, then lane 31 to the upper half.  No
+// LDS round trips (a shuffle-based scan waits on six of them).
+template <int kCtrl, int kRowMask>
+__device__ inline uint32_t dpp_moved(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, kRowMask, 0xF, false));
+}
+__device__ inline uint32_t wave_inclusive_scan(uint32_t x) {
+    x += dpp_moved<0x111, 0xF>(x);  // row_shr:1
+    x += dpp_moved<0x112, 0xF>(x);  // row_shr:2
+    x += dpp_moved<0x114, 0xF>(x);  // row_shr:4
+    x += dpp_moved<0x118, 0xF>(x);  // row_shr:8
+    x += dpp_moved<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_moved<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
 
@@ -264,14 +277,13 @@ struct SweepArgs {
     void *keys_out;
     const void *vals_in;
     void *vals_out;
-    const uint32_t *hist;    // this pass's digit counts of row 0; row r at hist + r * hist_row_stride
+    const uint32_t *bases;   // this pass's bucket bases of row 0; row r at bases + r * bases_row_stride
     void *status;            // [num_tiles][R] look-back words of this pass
     void *status_next;       // the next pass's words, cleared here (NULL on the last pass)
-    uint32_t *tile_counter;  // this pass's kXcds tile ticket counters, zero on entry
     uint32_t row_len;        // elements per row
     uint32_t tiles_per_row;
     uint32_t num_tiles;      // rows * tiles_per_row = grid size
-    uint32_t hist_row_stride;
+    uint32_t bases_row_stride;
     uint32_t shift;          // lowest bit of this pass's digit
     uint32_t digit_mask;     // (1 << width) - 1
     uint64_t flip;           // key transform masks (see KeyTraits)
@@ -286,40 +298,21 @@ struct SweepArgs {
     uint32_t part_tiles;
 };
 
-// Tile handed to the calling workgroup.  The tiles of a pass are dealt to the
-// XCDs in chunks of kXcdChunk consecutive tiles (chunk c to XCD c % kXcds), and
-// each XCD hands out its own chunks in order from its own counter; a workgroup
-// whose XCD has none left takes one from the next XCD's counter.  Neighbouring
-// tiles then mostly run on one XCD at the same time, so the cache lines that
-// their digit runs share are merged in that XCD's L2 instead of being written
-// back partially by two XCDs.  With one workgroup per tile every tile is taken
-// exactly once (a workgroup that found all counters exhausted would mean that
-// the other workgroups took every tile).  Returns num_tiles only if the grid
-// has more workgroups than tiles.
-__device__ inline uint32_t take_tile(uint32_t *counters, uint32_t num_tiles) {
-    const uint32_t xcd = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % kXcds;  // XCC_ID
-    for (uint32_t i = 0; i < kXcds; ++i) {
-        const uint32_t x = (xcd + i) % kXcds;
-        const uint32_t k = atomicAdd(counters + x, 1u);
-        const uint64_t tile = (static_cast<uint64_t>(k / kXcdChunk) * kXcds + x) * kXcdChunk + k % kXcdChunk;
-        if (tile < num_tiles) return static_cast<uint32_t>(tile);
-    }
-    return num_tiles;
-}
-
 // Workgroup-wide exclusive scan of one value per thread for a BLOCK-thread
 // workgroup.  Every thread must call it.  `tmp` holds BLOCK / 64 words of LDS.
-template <int BLOCK>
+// With kReuse false the caller does not touch `tmp` again before its next
+// barrier, so the trailing barrier that protects it is left out.
+template <int BLOCK, bool kReuse = true>
 __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int lane, int wave) {
     constexpr int WAVES = BLOCK / kWave;
-    const uint32_t inc = wave_inclusive_scan(v, lane);
+    const uint32_t inc = wave_inclusive_scan(v);
     if (lane == kWave - 1) tmp[wave] = inc;
     __syncthreads();
     uint32_t before = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w)
         if (w < wave) before += tmp[w];
-    __syncthreads();
+    if (kReuse) __syncthreads();
     return before + inc - v;
 }
 
@@ -349,7 +342,7 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
 // At least four waves per SIMD (two 512-thread workgroups per CU): the
 // partition loop would otherwise take 198 registers and halve that.
 template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, bool PART = false>
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void sweep_kernel(SweepArgs a) {
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP_WAVES_PER_EU))) void sweep_kernel(SweepArgs a) {
     constexpr uint32_t R = 1u << B;
     constexpr int WAVES = BLOCK / kWave;
     constexpr uint32_t TILE = BLOCK * ITEMS;
@@ -365,7 +358,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     __shared__ uint32_t s_cnt[WAVES][R];      // per-wave digit counts, then per-wave bases
     __shared__ uint32_t s_goff[R];            // output index of digit run start minus local start
     __shared__ uint32_t s_tmp[WAVES];
-    __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_gave_up;            // a look-back wave stopped waiting
 
     const int tid = threadIdx.x;
@@ -374,12 +366,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     // 64-bit look-back words also mark rows too long for 32-bit buffer offsets
     constexpr bool kWide = sizeof(W) == 8;
 
-    for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0])[i] = 0u;
-    if (!PART && tid == 0) {
-        s_ticket = take_tile(a.tile_counter, a.num_tiles);
-        s_gave_up = 0u;
-    }
-    __syncthreads();
+    // Each wave clears its own row of counters: only that wave touches it
+    // until the barrier after the ranking, and one wave's LDS accesses take
+    // effect in order, so no workgroup barrier is needed first.  (s_gave_up is
+    // read only after two barriers, and set only after the first.)
+    for (uint32_t d = lane; d < R; d += kWave) s_cnt[wave][d] = 0u;
+    if (!PART && tid == 0) s_gave_up = 0u;
 
     // Tiles are numbered row-major.  A tile waits below only for earlier tiles
     // of its row, and for a bounded number of polls (see the look-back).
@@ -390,10 +382,21 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         t_end = min(a.num_tiles, t_first + a.part_tiles);
         if (tid < static_cast<int>(R)) running = a.part_offsets[static_cast<uint64_t>(blockIdx.x) * R + tid];
     } else {
-        t_first = s_ticket;
+        // The tiles of a pass go to the XCDs in chunks of kXcdChunk consecutive
+        // tiles (chunk c to XCD c % kXcds); workgroup b runs on XCD b % kXcds,
+        // in order of b within its XCD, and takes that XCD's tiles in order.
+        // Neighbouring tiles then mostly run on one XCD at the same time, so
+        // the cache lines their digit runs share are merged in that XCD's L2
+        // instead of being written back partially by two.  The grid is whole
+        // rounds of kXcds * kXcdChunk workgroups, so every tile has exactly one
+        // (the extra workgroups find none).  A tile waits only for tiles before
+        // it, each XCD starts its tiles in order, and waits are bounded.
+        const uint32_t x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+        const uint64_t tile = (static_cast<uint64_t>(k / kXcdChunk) * kXcds + x) * kXcdChunk + k % kXcdChunk;
+        t_first = tile < a.num_tiles ? static_cast<uint32_t>(tile) : a.num_tiles;
         t_end = t_first + 1u;
     }
-    if (t_first >= a.num_tiles) return;  // not with zeroed counters and grid == num_tiles
+    if (t_first >= a.num_tiles) return;  // a workgroup of the last, partial round
     for (uint32_t t = t_first; t < t_end; ++t) {
         const uint32_t row = t / a.tiles_per_row;
         const uint32_t tile_in_row = t - row * a.tiles_per_row;
@@ -411,6 +414,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         Word key[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, wbase + j * kWave + lane);
+        // Digit d's first output index in the row (bucket base), thread d.
+        uint32_t bucket_base = 0u;
+        if (!PART && tid < static_cast<int>(R))
+            bucket_base = a.bases[static_cast<uint64_t>(row) * a.bases_row_stride + tid];
 
         // 2. Stable rank inside the wave; the group's lowest lane advances the
         // running count (and clears the mask).
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                 const uint32_t dig = digit_of<KK>(key[j], a.flip, a.flip_neg, a.shift, a.digit_mask);
                 const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
                 uint32_t below, size;
-                group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
+                group_rank(match_mask<B>(d), below, size);
                 const uint32_t before = s_cnt[wave][d];
                 rank[j] = (d << 16) | (before + below);
                 pin(rank[j]);
@@ -451,13 +458,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         if (!PART && tid < static_cast<int>(R))
             publish(status + tid, static_cast<W>((tile_in_row == 0 ? St::kInclusive : St::kAggregate) |
                                                  static_cast<W>(real)));
-        const uint32_t local_start = block_exclusive_scan_n<BLOCK>(count, s_tmp, lane, wave);
-        uint32_t bucket_base = 0u;
-        if constexpr (!PART) {
-            const uint32_t hcount = (tid < static_cast<int>(R))
-                ? a.hist[static_cast<uint64_t>(row) * a.hist_row_stride + tid] : 0u;
-            bucket_base = block_exclusive_scan_n<BLOCK>(hcount, s_tmp, lane, wave);
-        }
+        // (s_tmp is written again only by the next tile, after three barriers)
+        const uint32_t local_start = block_exclusive_scan_n<BLOCK, false>(count, s_tmp, lane, wave);
         if (tid < static_cast<int>(R)) {
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
@@ -473,15 +475,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
             rank[j] = slot;
         }
 
-        // Payload loads go out now, with the keys out of the registers, and are
-        // in flight while the look-back waits.
-        uint32_t val[ITEMS];
-        if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
-            const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
-            const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
-        }
+
 
         // Look-back walk, one thread per digit.  Each round trip a lane reads its
         // digit's words of the next kLookback predecessors (nearest first) and adds
@@ -541,29 +535,34 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                     }
                 }
             }
+            // The digits a wave found publish their inclusive counts and run
+            // starts at once.  If any wave gave up (or no wave looked back), the
+            // barrier makes that visible and the workgroup counts every digit
+            // over the earlier tiles' keys, which gives the same prefixes, and
+            // sets (and publishes) them all again.
+            auto finish = [&](W prefix) {
+                if (tile_in_row != 0) publish(status + tid, static_cast<W>(St::kInclusive | (prefix + real)));
+                s_goff[tid] = bucket_base + static_cast<uint32_t>(prefix) - local_start;
+                if (a.status_next != nullptr) static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
+            };
             if (gave_up && lane == 0) s_gave_up = 1u;
+            if (!from_keys && !gave_up && tid < static_cast<int>(R)) finish(excl);
             __syncthreads();
             if (from_keys || s_gave_up != 0u) {
-                if (tid < static_cast<int>(R)) s_goff[tid] = 0u;
+                uint32_t *cnt = &s_cnt[0][0];  // free once the tile is reordered
+                if (tid < static_cast<int>(R)) cnt[tid] = 0u;
                 __syncthreads();
                 const Stored *row_keys = static_cast<const Stored *>(a.keys_in) + row_base;
                 for (uint32_t i = tid; i < tile_start; i += BLOCK) {
                     const uint32_t d = digit_of<KK>(row_keys[i], a.flip, a.flip_neg, a.shift, a.digit_mask);
-                    atomicAdd(&s_goff[d], 1u);
+                    atomicAdd(&cnt[d], 1u);
                 }
                 __syncthreads();
-                if (tid < static_cast<int>(R)) excl = s_goff[tid];
+                if (tid < static_cast<int>(R)) finish(cnt[tid]);
                 __syncthreads();
             }
-            if (tid < static_cast<int>(R)) {
-                if (tile_in_row != 0)
-                    publish(status + tid, static_cast<W>(St::kInclusive | (excl + real)));
-                s_goff[tid] = bucket_base + static_cast<uint32_t>(excl) - local_start;
-                if (a.status_next != nullptr)
-                    static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
-            }
         }
-        __syncthreads();
+        if constexpr (PART) __syncthreads();
 
         // 5. Keys out: slot k goes to s_goff[d] + k.  That is below row_len for
         // every real element; the range check of the buffer store only keeps a
@@ -574,8 +573,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         for (int i = 0; i < (ITEMS + 3) / 4; ++i) slot_digits[i] = 0u;
         const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
         // Without the bounds select (full tiles) the loop has no branches and
-        // all of a thread's slot reads can be in flight at once.  Only keys-only
-        // sorts take that copy: with a payload it measured slower.
+        // all of a thread's slot reads can be in flight at once.
         auto keys_out = [&](auto partial) {
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
@@ -593,11 +591,18 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                 }
             }
         };
-        if constexpr (PK == kPayNone) {
-            if (valid == TILE) keys_out(std::false_type{});
-            else keys_out(std::true_type{});
-        } else {
-            keys_out(std::true_type{});
+        if (valid == TILE) keys_out(std::false_type{});
+        else keys_out(std::true_type{});
+
+        // The payload is loaded only now, after the keys have gone out (loading
+        // it before the look-back, to overlap that wait, measured 0.3% slower on
+        // uniform 2^28 pairs and 4% slower with AND-of-3 keys).
+        uint32_t val[ITEMS];
+        if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
+            const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
+            const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
         }
 
         if constexpr (PK != kPayNone) {
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(BLOCK) void resident_sort_kernel(ResidentArgs a) {
             const uint32_t p = wbase + j * kWave + lane;
             const uint32_t d = (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip, a.flip_neg) >> shift) & mask) : (R - 1u);
             uint32_t below, size;
-            group_rank_from_mismatch(mismatch_mask<B>(d), lane, below, size);
+            group_rank(match_mask<B>(d), below, size);
             const uint32_t before = s_cnt[wave][d];
             rank[j] = (d << 16) | (before + below);
             pin(rank[j]);
@@ -777,6 +782,167 @@ __global__ __launch_bounds__(BLOCK) void resident_sort_kernel(ResidentArgs a) {
     }
 }
 
+// ---------------------------------------- whole-row sort of 16-bit keys
+
+struct RowResidentArgs {
+    const uint16_t *keys_in;   // rows x row_len fp16/bf16 patterns
+    uint16_t *keys_out;
+    const uint32_t *pay_in;    // rows x row_len u32 payload (kResU32), else unused
+    void *pay_out;             // int64 column index (kResIndex) or u32 payload (kResU32)
+    uint32_t rows;
+    uint32_t row_len;          // at most BLOCK * ITEMS
+    uint32_t flip;             // 0xFFFF: descending
+};
+
+// Order-preserving key of a 16-bit float pattern and its inverse (negative
+// patterns complemented, non-negative ones with the sign bit set; `flip`
+// complements the key for descending order).
+__device__ inline uint32_t f16_key(uint32_t v, uint32_t flip) {
+    return (v ^ ((v & 0x8000u) ? 0xFFFFu : 0x8000u)) ^ flip;
+}
+__device__ inline uint32_t f16_pattern(uint32_t key, uint32_t flip) {
+    const uint32_t asc = (key ^ flip) & 0xFFFFu;
+    return (asc & 0x8000u) ? (asc ^ 0x8000u) : (~asc & 0xFFFFu);
+}
+
+// Sorts whole rows of 16-bit float patterns inside LDS, all passes of the
+// 16-bit key, one row at a time per workgroup (workgroups loop over rows).
+//
+// Each element travels as one word, key << 16 | column: the key is computed
+// once per row, the column (< 2^16) is the payload, and one LDS buffer holds
+// the row between passes.  Slots past the row end hold key 0xFFFF and their
+// own position, so in every pass they take the largest digit, rank after every
+// real element and are never written out: no pass needs a bounds test.
+//
+// Per pass: wave ballots rank each word among the words of its digit in its
+// wave (lanes of one wave hold consecutive elements, item by item, so (item,
+// lane) order is input order), the per-wave digit counts are scanned into
+// digit starts, and the words move to their slots of the pass's order in LDS.
+// After the last pass the row is in order: values and column indices go out
+// with consecutive threads on consecutive slots.
+//
+// The next row's keys are loaded into registers before the current row is
+// ranked, so HBM reads of one row and writes of the previous one overlap the
+// ranking of the current one.
+#ifndef LRS_ROW_WAVES_PER_EU
+#define LRS_ROW_WAVES_PER_EU 6
+#endif
+#ifndef LRS_ROW_PREFETCH
+#define LRS_ROW_PREFETCH 1
+#endif
+template <int B, int ITEMS, int BLOCK, int PK>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_ROW_WAVES_PER_EU))) void row_resident_kernel(RowResidentArgs a) {
+    constexpr uint32_t R = 1u << B;
+    constexpr int WAVES = BLOCK / kWave;
+    constexpr uint32_t TILE = BLOCK * ITEMS;
+    static_assert(BLOCK % kWave == 0 && BLOCK >= static_cast<int>(R), "one thread per digit");
+    static_assert(TILE <= 65536, "columns must fit in 16 bits");
+    __shared__ uint32_t s_w[TILE];
+    __shared__ uint32_t s_cnt[2][WAVES][R];  // pass p counts in table p & 1 and clears the other
+    __shared__ uint32_t s_tmp[WAVES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t n = a.row_len;
+    const uint32_t wbase = static_cast<uint32_t>(wave) * kWave * ITEMS;
+    static_assert((16 / B) % 2 == 0, "an even number of passes leaves table 0 cleared for the next row");
+
+    uint32_t row = blockIdx.x;
+    if (row >= a.rows) return;
+    uint32_t raw[ITEMS];
+    auto load_row = [&](uint32_t r) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.keys_in + static_cast<uint64_t>(r) * n, n * 2u);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) raw[j] = BufIO<uint16_t>::load(rs, wbase + j * kWave + lane);
+    };
+    if (LRS_ROW_PREFETCH) load_row(row);
+    for (uint32_t i = tid; i < WAVES * R; i += BLOCK) (&s_cnt[0][0][0])[i] = 0u;
+    __syncthreads();
+
+    for (; row < a.rows; row += gridDim.x) {
+        if (!LRS_ROW_PREFETCH) load_row(row);
+        uint32_t w[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t p = wbase + j * kWave + lane;
+            w[j] = ((p < n) ? (f16_key(raw[j], a.flip) << 16) : 0xFFFF0000u) | p;
+        }
+        if (LRS_ROW_PREFETCH && row + gridDim.x < a.rows) load_row(row + gridDim.x);
+
+#pragma unroll 1
+        for (uint32_t shift = 0; shift < 16u; shift += B) {
+            const int t = (shift / B) & 1;
+            if (shift != 0) {
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) w[j] = s_w[wbase + j * kWave + lane];
+            }
+
+            uint32_t rank[ITEMS];  // rank within the wave's digit
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t d = __builtin_amdgcn_ubfe(w[j], 16u + shift, B);
+                uint32_t below, size;
+                group_rank(match_mask<B>(d), below, size);
+                const uint32_t before = s_cnt[t][wave][d];
+                rank[j] = before + below;
+                pin(rank[j]);
+                if (below == 0u) s_cnt[t][wave][d] = before + size;
+            }
+            __syncthreads();
+
+            // Digit d is owned by thread d: per-wave counts become per-wave
+            // starts, and the other table is cleared for the next pass.
+            uint32_t count = 0u;
+            if (tid < static_cast<int>(R)) {
+#pragma unroll
+                for (int v = 0; v < WAVES; ++v) {
+                    const uint32_t c = s_cnt[t][v][tid];
+                    s_cnt[t][v][tid] = count;
+                    s_cnt[t ^ 1][v][tid] = 0u;
+                    count += c;
+                }
+            }
+            const uint32_t start = block_exclusive_scan_n<BLOCK, false>(count, s_tmp, lane, wave);
+            if (tid < static_cast<int>(R)) {
+#pragma unroll
+                for (int v = 0; v < WAVES; ++v) s_cnt[t][v][tid] += start;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j)
+                s_w[s_cnt[t][wave][__builtin_amdgcn_ubfe(w[j], 16u + shift, B)] + rank[j]] = w[j];
+            __syncthreads();
+        }
+
+        // The row in order: slot k holds the k-th element.
+        const uint64_t row_base = static_cast<uint64_t>(row) * n;
+        const __amdgpu_buffer_rsrc_t kout = make_rsrc(a.keys_out + row_base, n * 2u);
+        if constexpr (PK == kResIndex) {
+            const __amdgpu_buffer_rsrc_t iout = make_rsrc(static_cast<int64_t *>(a.pay_out) + row_base, n * 8u);
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t k = i * BLOCK + tid;
+                const uint32_t v = s_w[k];
+                BufIO<uint16_t>::store(kout, k, f16_pattern(v >> 16, a.flip));
+                BufIO<int64_t>::store(iout, k, v & 0xFFFFu);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t pin_r = make_rsrc(a.pay_in + row_base, n * 4u);
+            const __amdgpu_buffer_rsrc_t pout = make_rsrc(static_cast<uint32_t *>(a.pay_out) + row_base, n * 4u);
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t k = i * BLOCK + tid;
+                const uint32_t v = s_w[k];
+                BufIO<uint16_t>::store(kout, k, f16_pattern(v >> 16, a.flip));
+                // the payload of the element from column v & 0xFFFF (slots past
+                // the row end read 0 and are not stored)
+                BufIO<uint32_t>::store(pout, k, BufIO<uint32_t>::load(pin_r, v & 0xFFFFu));
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------- digit histograms
 
 struct HistArgs {
@@ -790,6 +956,8 @@ struct HistArgs {
     uint64_t flip;           // key transform masks (see KeyTraits)
     uint64_t flip_neg;
     uint32_t atomic;         // 1: several workgroups per row accumulate; 0: one writes it
+    uint32_t *bases;         // [rows][passes][R] bucket bases written by the row's last workgroup, or NULL
+    uint32_t *done;          // [rows] workgroups finished per row, zero on entry (atomic only)
 };
 
 constexpr int kHistMaxCounters = 2048;  // passes * R for every legal (window, b, key width)
@@ -891,20 +1059,63 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
         count_key(static_cast<Word>(base[body_end + threadIdx.x]));
     __syncthreads();
 
-    uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
-    for (uint32_t i = threadIdx.x; i < total; i += kHistBlock) {
+    // this workgroup's count of counter i (copies taken in a rotated order so
+    // neighbouring threads read different banks)
+    auto lds_count = [&](uint32_t i) {
         const uint32_t p = i / R, d = i - p * R;
         uint32_t c = 0;
-        // copies taken in a rotated order so neighbouring threads read different banks
 #pragma unroll
         for (int k = 0; k < kCopies; ++k)
             c += s_h[p * kPassWords + d * kCopies + ((k + i) % kCopies)];
+        return c;
+    };
+    uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
+    for (uint32_t i = threadIdx.x; i < total; i += kHistBlock) {
+        const uint32_t c = lds_count(i);
         if (a.atomic) {
             if (c) atomicAdd(out + i, c);
         } else {
             out[i] = c;
         }
     }
+    if (a.bases == nullptr) return;
+
+    // The bucket bases: the exclusive scan of each pass's counts.  The last
+    // workgroup of the row to finish has every count.  The barrier orders this
+    // workgroup's count additions before one thread's acquire-release count of
+    // finished workgroups; the last one's acquire orders every workgroup's
+    // additions before its reads.
+    __shared__ uint32_t s_last;
+    if (a.atomic) {
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(a.done + row, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                     a.chunks_per_row - 1 ? 1u : 0u;
+        __syncthreads();
+        if (s_last == 0u) return;
+    }
+    // Thread i scans counts 2i and 2i+1 (R is even, so every pass starts at an
+    // even index); one scan runs over all passes at once and each pass then
+    // subtracts the prefix at its first digit (exact modulo 2^32).
+    static_assert(2 * kHistBlock >= kHistMaxCounters, "two counts per thread cover every pass");
+    uint32_t c0 = 0u, c1 = 0u;
+    const uint32_t i0 = 2u * threadIdx.x;
+    auto final_count = [&](uint32_t i) -> uint32_t {
+        if (i >= total) return 0u;
+        return a.atomic ? __hip_atomic_load(out + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lds_count(i);
+    };
+    c0 = final_count(i0);
+    c1 = final_count(i0 + 1u);
+    __shared__ uint32_t s_scan[kHistBlock / kWave];
+    __shared__ uint32_t s_pass_start[kHistMaxCounters / 2];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const uint32_t e0 = block_exclusive_scan_n<kHistBlock, false>(c0 + c1, s_scan, lane, wave);
+    if (i0 < total && i0 % R == 0) s_pass_start[i0 / R] = e0;
+    __syncthreads();
+    uint32_t *bases = a.bases + static_cast<uint64_t>(row) * total;
+    if (i0 < total) bases[i0] = e0 - s_pass_start[i0 / R];
+    if (i0 + 1u < total) bases[i0 + 1u] = e0 + c0 - s_pass_start[i0 / R];
 }
 
 // --------------------------------------------- reduce-then-scan, per pass

@@ -41,8 +41,13 @@ hipError_t launch_hist(int b, const HistArgs &a, uint32_t blocks, hipStream_t s)
 template <int KK>
 hipError_t launch_partition_counts(int b, const PartArgs &pa, hipStream_t s);
 
-// Whole-row resident sort, one workgroup per row.
+// Whole-row resident sort, one workgroup per row (32- and 64-bit keys).
 template <int KK, int PK>
 hipError_t launch_resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s);
+
+// Whole-row sort of 16-bit float rows: as many workgroups as fit on the GPU at
+// once (at most one per row), each looping over rows.
+template <int PK>
+hipError_t launch_row_resident(int b, const RowResidentArgs &a, hipStream_t s);
 
 }  // namespace lrs

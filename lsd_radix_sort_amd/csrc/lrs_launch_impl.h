@@ -3,12 +3,18 @@
 // them (and so compile the kernels) for one key kind each.
 #pragma once
 
+#include <atomic>
+
 #include "lrs_launch.h"
 
 namespace lrs {
 
 template <int B, int ITEMS, int BLOCK, int KK, int PK, typename W, bool PART>
 void launch_sweep_cfg(const SweepArgs &a, uint64_t grid_size, hipStream_t s) {
+    // look-back sweeps map tiles from the workgroup index in whole rounds of
+    // kXcds * kXcdChunk workgroups (see sweep_kernel); the extra ones return
+    constexpr uint64_t round = uint64_t(kXcds) * kXcdChunk;
+    if (!PART) grid_size = (grid_size + round - 1) / round * round;
     const dim3 grid(static_cast<uint32_t>(grid_size));
     sweep_kernel<B, ITEMS, BLOCK, KK, PK, W, PART><<<grid, BLOCK, 0, s>>>(a);
 }
@@ -85,6 +91,59 @@ hipError_t launch_resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t
         default: launch_resident_b<8, KK, PK>(a, rows, row_len, s); break;
     }
     return hipGetLastError();
+}
+
+// Workgroups of `kernel` that fit on the current GPU at once (compute units x
+// the occupancy per unit), queried once per device and kernel and kept, so a
+// call under graph capture makes no query.  0 if the runtime cannot tell.
+template <typename Kernel>
+uint32_t resident_capacity(Kernel kernel, int block) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<uint32_t> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    uint32_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || cus <= 0 ||
+        per_cu <= 0)
+        return 0;
+    c = static_cast<uint32_t>(cus) * static_cast<uint32_t>(per_cu);
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+template <int B, int ITEMS, int BLOCK, int PK>
+hipError_t launch_row_resident_cfg(const RowResidentArgs &a, hipStream_t s) {
+    auto kernel = row_resident_kernel<B, ITEMS, BLOCK, PK>;
+    const uint32_t cap = resident_capacity(kernel, BLOCK);
+    const uint32_t grid = (cap == 0 || cap > a.rows) ? a.rows : cap;
+    kernel<<<dim3(grid), BLOCK, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+#ifndef LRS_ROW_ITEMS
+#define LRS_ROW_ITEMS 8
+#endif
+template <int B, int PK>
+hipError_t launch_row_resident_b(const RowResidentArgs &a, hipStream_t s) {
+    // the smallest shape that holds the row
+    constexpr int I = LRS_ROW_ITEMS;
+    static_assert(1024 * I >= 8192, "the largest shape holds a row of 8192");
+    if (a.row_len <= 256u * I) return launch_row_resident_cfg<B, I, 256, PK>(a, s);
+    if (a.row_len <= 512u * I) return launch_row_resident_cfg<B, I, 512, PK>(a, s);
+    return launch_row_resident_cfg<B, I, 1024, PK>(a, s);
+}
+
+template <int PK>
+hipError_t launch_row_resident(int b, const RowResidentArgs &a, hipStream_t s) {
+    switch (b) {
+        case 1: return launch_row_resident_b<1, PK>(a, s);
+        case 2: return launch_row_resident_b<2, PK>(a, s);
+        case 4: return launch_row_resident_b<4, PK>(a, s);
+        default: return launch_row_resident_b<8, PK>(a, s);
+    }
 }
 
 }  // namespace lrs
