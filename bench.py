@@ -7,7 +7,8 @@ already resident in HBM, out of place from an input the loop never writes.
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--scan lookback|reduce-then-scan] [--lib PATH]
+    python bench.py --graph-sweep     (eager vs HIP-graph replay, 1K .. 1M keys)
 
 Other workloads (same line format, for the record): c1_keys_1k_4bit,
 c2_keys_4m_4bit, c2_keys_4m_8bit, c3_pairs_2p28_and3, c4_fp16_1024x65536_asc,
@@ -166,6 +167,67 @@ def cpu_baseline(min_seconds: float = 10.0, max_runs: int = 3):
     }
 
 
+def graph_sweep(sizes, digit_bits: int, reps: int):
+    """Per-sort time of u32 keys-only sorts launched eagerly and replayed from a
+    captured HIP graph, at each size; prints a markdown table to stderr and
+    returns the rows."""
+    import numpy as np
+    import torch
+
+    import lsd_radix_sort_amd as lrs
+    import workloads
+
+    rows = []
+    log(f"| keys | launches per sort | eager us/sort | graph replay us/sort | graph / eager |")
+    log("|---:|---:|---:|---:|---:|")
+    for n in sizes:
+        keys = workloads.random_u32(20_000 + n % 997, n)
+        k_in = torch.from_numpy(keys.view(np.int32)).cuda()
+        k_out = torch.empty_like(k_in)
+        ws = torch.empty(max(1, lrs.radix_sort_workspace_size(n, 0, 32, digit_bits)), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            lrs.radix_sort_keys(k_in, 0, 32, digit_bits, out=k_out, workspace=ws)
+
+        timer = lrs.KernelTimer()
+        lrs.radix_sort_keys(k_in, 0, 32, digit_bits, out=k_out, workspace=ws,
+                            options=lrs.SortOptions(timer=timer))
+        torch.cuda.synchronize()
+        launches = sum(timer.read()[1].values())
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        result = {}
+        for mode in ("eager", "graph"):
+            call = run if mode == "eager" else g.replay
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                call()
+            t1.record()
+            torch.cuda.synchronize()
+            result[mode] = t0.elapsed_time(t1) * 1e3 / reps
+        got = k_out.cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, np.sort(keys)), f"n={n}: sort result wrong"
+        row = {"n": n, "launches": launches, "eager_us": round(result["eager"], 2),
+               "graph_us": round(result["graph"], 2), "ratio": round(result["graph"] / result["eager"], 3)}
+        rows.append(row)
+        log(f"| {n:,} | {launches} | {row['eager_us']} | {row['graph_us']} | {row['ratio']} |")
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,11 +239,31 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scan", default="lookback", choices=["lookback", "reduce-then-scan"],
                     help="offset strategy of single-row sorts (the A/B of the two)")
+    ap.add_argument("--graph-sweep", action="store_true",
+                    help="instead of the workload: eager vs HIP-graph replay per-sort time of u32 keys-only "
+                         "sorts from 1K to 1M keys (table on stderr, one JSON line)")
+    ap.add_argument("--lib", default=None,
+                    help="library file to time instead of the in-tree build (a variant built with "
+                         "python -m lsd_radix_sort_amd.build -D... --out PATH)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    if args.graph_sweep:
+        import torch
+
+        import lsd_radix_sort_amd as lrs
+        if args.lib is not None:
+            lrs.LIB_PATH = os.path.abspath(args.lib)
+        lrs.load_library()
+        out = {}
+        for b in (4, 8):
+            log(f"u32 keys only, {32 // b} passes of {b}-bit digits")
+            out[f"b{b}"] = graph_sweep([1024, 4096, 16384, 65536, 262144, 1 << 20], b, max(args.steps, 50))
+        print(json.dumps({"metric": "per-sort time, eager launches vs HIP-graph replay", "unit": "us",
+                          "graph_sweep": out}), flush=True)
+        return
     name = args.workload
     if args.dist is not None:
         name = f"c3_pairs_2p28_{args.dist}"
@@ -194,6 +276,8 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.lib is not None:
+        lrs.LIB_PATH = os.path.abspath(args.lib)
     lrs.load_library()
     dev = torch.device("cuda:0")
     timer = lrs.KernelTimer()
@@ -335,14 +419,15 @@ def main():
         "dtype": "u16" if w["kind"] == "rows" else ("u64" if w.get("key_bytes", 4) == 8 else "u32"),
         "data": "synthetic",
         "config": {"workload": w["desc"], "name": name, "n": n_keys, "digit_bits": w["b"],
-                   "passes": launches_per_sort, "scan": args.scan},
+                   "passes": launches_per_sort, "scan": args.scan,
+                   **({"lib": os.path.basename(args.lib)} if args.lib else {})},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(name) if args.scan == "lookback" else None,
+            "traffic": measured_traffic(name) if args.scan == "lookback" and args.lib is None else None,
             "kernel": "resident_sort_kernel (whole row, all passes in LDS)" if resident
                       else "sweep_kernel (one LSD pass)",
             "bytes_per_launch": bytes_sort // max(launches_per_sort, 1),

@@ -1,10 +1,16 @@
 """Build the gfx950 shared library in-tree with hipcc.
 
-    python -m lsd_radix_sort_amd.build [-v] [-j N]
+    python -m lsd_radix_sort_amd.build [-v] [-j N] [-DNAME=VALUE ...] [--out PATH]
 
 Each csrc/*.hip translation unit (the driver and C ABI, and one unit per key
 kind holding that kind's kernels) compiles to an object in parallel; the
 objects link into lsd_radix_sort_amd/liblsd_radix_sort.so.  Always recompiles.
+
+-D options set the compile-time tunables of csrc/lrs_kernels.h (tile shape,
+look-back window, XCD chunk, ...) in every unit; with --out the library is
+written elsewhere, so a variant can be timed beside the default with
+``bench.py --lib PATH`` (the A/B measurements of the design notes are made
+this way).
 """
 from __future__ import annotations
 
@@ -72,7 +78,12 @@ def build(verbose: bool = False, jobs: int | None = None, extra_flags: list[str]
 
 
 if __name__ == "__main__":
+    argv = sys.argv[1:]
     j = None
-    if "-j" in sys.argv:
-        j = int(sys.argv[sys.argv.index("-j") + 1])
-    print(build(verbose="-v" in sys.argv, jobs=j))
+    out = LIB
+    defines = [a for a in argv if a.startswith("-D")]
+    if "-j" in argv:
+        j = int(argv[argv.index("-j") + 1])
+    if "--out" in argv:
+        out = os.path.abspath(argv[argv.index("--out") + 1])
+    print(build(verbose="-v" in argv, jobs=j, extra_flags=defines, out=out))
