@@ -1,8 +1,8 @@
 """Oracle vs textbook/library stable sorts, invariants and cross-width agreement.
 
 Python's sorted() and numpy's argsort(kind="stable") are stable comparison sorts,
-independent of the oracle's counting passes.  The exhaustive case covers every
-sequence of up to 4 keys over 4 bits for each digit width that divides the
+independent of the oracle's counting passes.  The exhaustive cases cover every
+sequence of up to 5 keys over 4 bits for each digit width that divides the
 window; the random cases cover windows that do not start at 0 or divide evenly.
 """
 import itertools
@@ -30,6 +30,23 @@ def test_exhaustive_small_sequences(b):
             order = sorted(range(n), key=lambda i: seq[i])
             assert vo.tolist() == order, (seq, b)
             assert ko.tolist() == [seq[i] for i in order]
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+@pytest.mark.parametrize("descending", [False, True])
+def test_exhaustive_five_key_sequences(b, descending):
+    """Every sequence of 5 keys over 4 bits (16^5 = 1,048,576 of them), each
+    sorted on its own by the oracle's LSD passes: the sequences are the rows of
+    a matrix whose entries are fp16 patterns 0x3C00 + v (1 + v/1024, ordered
+    like v), and the row sort runs the counting-pass sort per row over the
+    16-bit key.  numpy's stable argsort along each row is the reference."""
+    m = 16 ** 5
+    seq = ((np.arange(m)[:, None] >> (4 * np.arange(4, -1, -1))[None, :]) & 15).astype(np.int64)
+    bits = (0x3C00 + seq).astype(np.uint16)
+    vals, idx = oracle.segmented_row_sort(bits, descending, b)
+    order = np.argsort(-seq if descending else seq, axis=1, kind="stable")
+    assert np.array_equal(idx, order), f"b={b} descending={descending}: an index order differs"
+    assert np.array_equal(vals, np.take_along_axis(bits, order, axis=1))
 
 
 def test_random_windows_all_widths():
