@@ -104,8 +104,13 @@ def sweep_bytes(w) -> int:
     n = w["rows"] * w["cols"]
     total = 0
     for p in range(P):
-        read = 2 + (4 if p > 0 else 0)          # 16-bit pattern (+ u32 index after the first pass)
-        write = 2 + (8 if p == P - 1 else 4)    # pattern + u32 index (int64 on the last pass)
+        if w["cols"] <= 65536:
+            # key << 16 | column as one u32 word between passes
+            read = 2 if p == 0 else 4           # pattern, then words
+            write = 2 + 8 if p == P - 1 else 4  # words, then pattern + int64 index
+        else:
+            read = 2 + (4 if p > 0 else 0)          # 16-bit pattern (+ u32 index after the first pass)
+            write = 2 + (8 if p == P - 1 else 4)    # pattern + u32 index (int64 on the last pass)
         total += read + write
     return n * total
 

@@ -107,13 +107,16 @@ namespace {
 constexpr uint64_t kMinTiles = LRS_MIN_TILES;
 // Rows up to this length are sorted whole inside one workgroup's LDS.
 constexpr uint64_t kResidentMax = 8192;
+// Longer index row sorts of rows up to this length carry each element as one
+// 32-bit word, key << 16 | column, between passes.
+constexpr uint64_t kPackedRowMax = 65536;
 
 // The largest tile shape with at least kMinTiles tiles and at most 1/32 of
 // its elements past row ends (rows of 65536 take eight 8192-key tiles, not
 // five 15360-key tiles with 15% padding).
-int choose_tile_cfg(uint64_t rows, uint64_t row_len, bool key64) {
+int choose_tile_cfg(uint64_t rows, uint64_t row_len, bool key64, bool keys_only) {
     for (int c = 2; c >= 1; --c) {
-        const uint64_t tile = tile_cfg_of(key64, c).tile;
+        const uint64_t tile = tile_cfg_of(key64, c, keys_only).tile;
         const uint64_t tiles = rows * ((row_len + tile - 1) / tile);
         const uint64_t padded = tiles * tile;
         if (tiles >= kMinTiles && (padded - rows * row_len) * 32 <= padded) return c;
@@ -195,6 +198,8 @@ struct Plan {
     uint32_t tiles_per_row = 0;
     uint64_t num_tiles = 0;
     bool wide_status = false;       // 64-bit look-back words and store addresses (see make_plan)
+    bool keys_only = false;         // sweeps with no payload phase (their own tile shapes)
+    bool packed = false;            // row sort carrying key << 16 | column words between passes
     uint32_t hist_chunks_per_row = 0;
     // workspace layout (byte offsets)
     uint64_t off_hist = 0, hist_words = 0;
@@ -205,12 +210,12 @@ struct Plan {
     uint64_t total = 0;
 };
 
-// kind: 0 keys, 1 pairs, 2 segmented
 // kind: 0 keys, 1 pairs, 2 segmented; key_bytes: 4 or 8 (segmented keys are 2 bytes)
 // wide_from: nonzero sends rows of at least that many elements (sorted by
-// sweeps) to the wide sweep as well.
+// sweeps) to the wide sweep as well.  row_index: a segmented sort whose
+// payload is the column index the kernels make (not a caller's payload).
 Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int b, int kind, int key_bytes = 4,
-               uint64_t wide_from = 0) {
+               uint64_t wide_from = 0, bool row_index = true) {
     Plan p;
     const bool key64 = key_bytes == 8;
     p.rows = rows;
@@ -229,9 +234,11 @@ Plan make_plan(uint64_t rows, uint64_t row_len, int begin_bit, int end_bit, int 
     p.wide_status = row_len * widest >= (1ull << 32) || row_len >= (1ull << 30);
     const bool resident = row_len <= kResidentMax && !key64;
     if (wide_from != 0 && row_len >= wide_from && !resident) p.wide_status = true;
+    p.packed = kind == 2 && row_index && row_len <= kPackedRowMax && !p.wide_status;
+    p.keys_only = !key64 && (kind == 0 || p.packed);
     // the wide sweep exists for the largest tile shape only
-    p.tile_cfg = p.wide_status ? 2 : choose_tile_cfg(rows, row_len, key64);
-    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, tile_cfg_of(key64, p.tile_cfg).tile));
+    p.tile_cfg = p.wide_status ? 2 : choose_tile_cfg(rows, row_len, key64, p.keys_only);
+    p.tiles_per_row = static_cast<uint32_t>(cdiv(row_len, tile_cfg_of(key64, p.tile_cfg, p.keys_only).tile));
     p.num_tiles = rows * p.tiles_per_row;
 
     // histogram: about kHistTargetBlocks workgroups in all, at least
@@ -441,7 +448,7 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
         pa.keys = src_k;
         pa.counts = counts;
         pa.n = static_cast<uint32_t>(p.row_len);
-        pa.part_len = static_cast<uint32_t>(part_tiles * tile_cfg_of(false, p.tile_cfg).tile);
+        pa.part_len = static_cast<uint32_t>(part_tiles * tile_cfg_of(false, p.tile_cfg, p.keys_only).tile);
         pa.partitions = static_cast<uint32_t>(partitions);
         pa.shift = a.shift;
         pa.digit_mask = a.digit_mask;
@@ -645,7 +652,7 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
     if (st != LRS_OK) return st;
     if (rows == 0 || n == 0) return LRS_OK;
     const bool index = pay_in == nullptr;
-    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2, 4, c.wide_from);
+    const Plan p = make_plan(rows, n, 0, 16, digit_bits, 2, 4, c.wide_from, index);
     if (!vals_in || !vals_out || !pay_out || (p.total && !workspace)) return LRS_ERR_NULL_POINTER;
     const uint64_t pay_size = index ? 8 : 4;
     if (misaligned(vals_in, 2) || misaligned(vals_out, 2) || misaligned(pay_out, pay_size) ||
@@ -687,6 +694,39 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
     uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
     uint32_t *idx[2] = {reinterpret_cast<uint32_t *>(ws + p.off_idx[0]),
                         reinterpret_cast<uint32_t *>(ws + p.off_idx[1])};
+    if (p.packed) {
+        // Key and column travel as one word, key << 16 | column: the first
+        // pass makes the words, the middle passes sort them by their high
+        // half, the last pass writes the patterns and int64 columns back.
+        // Each element moves 4 bytes between passes instead of 2 + 4, and no
+        // pass but the last has a separate payload phase.
+        const uint32_t *src_w = nullptr;
+        for (int pass = 0; pass < p.passes; ++pass) {
+            SweepArgs a = pass_args(p, ws, pass, c);
+            a.flip = flip;
+            uint32_t *dw = idx[pass & 1];
+            hipError_t e;
+            TimedLaunch t(2, c);
+            if (pass == 0) {
+                a.keys_in = vals_in;
+                a.keys_out = dw;
+                e = launch_sweep<kKeyF16, kPayPackFirst, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, c.s);
+            } else {
+                // the words' digit fields sit 16 bits above the key's
+                a.shift += 16;
+                a.keys_in = src_w;
+                const bool last = pass + 1 == p.passes;
+                a.keys_out = last ? static_cast<void *>(vals_out) : static_cast<void *>(dw);
+                a.vals_out = last ? pay_out : nullptr;
+                e = last ? launch_sweep<kKeyU32, kPayUnpackLast, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, c.s)
+                         : launch_sweep<kKeyU32, kPayNone, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, c.s);
+            }
+            t.done();
+            if (e != hipSuccess) return LRS_ERR_HIP;
+            src_w = dw;
+        }
+        return LRS_OK;
+    }
     const uint16_t *src_k = vals_in;
     const uint32_t *src_p = pay_in;
     for (int pass = 0; pass < p.passes; ++pass) {
@@ -799,7 +839,9 @@ int radix_sort_pairs_typed(const void *keys_in, const uint32_t *vals_in, void *k
 size_t segmented_row_sort_workspace_size(int64_t rows, int64_t n, int digit_bits, const lrs_options *opts) {
     if (!options_ok(opts) || check_rows(rows, n, LRS_DTYPE_FP16, digit_bits) != LRS_OK || rows == 0 || n == 0)
         return 0;
-    return static_cast<size_t>(make_plan(rows, n, 0, 16, digit_bits, 2, 4, wide_from_of(opts)).total);
+    // one size for both row sorts (index or caller payload)
+    return static_cast<size_t>(std::max(make_plan(rows, n, 0, 16, digit_bits, 2, 4, wide_from_of(opts), true).total,
+                                        make_plan(rows, n, 0, 16, digit_bits, 2, 4, wide_from_of(opts), false).total));
 }
 
 int segmented_row_sort(const uint16_t *vals_in, uint16_t *vals_out, int64_t *idx_out, int64_t rows, int64_t n,

@@ -1,5 +1,5 @@
 // lrs_kernels.h -- gfx950 device code of the LSD radix sort (internal header,
-// included by lrs_host.hip only).
+// included through lrs_launch.h; the lrs_inst_*.hip units compile it).
 //
 // One pass of the sort is one launch of `sweep_kernel`: every workgroup takes
 // the next tile of TILE keys in input order, ranks each key stably inside the
@@ -29,6 +29,9 @@ namespace lrs {
 #ifndef LRS_SWEEP_ITEMS
 #define LRS_SWEEP_ITEMS 30      // keys per thread in the largest sweep tile
 #endif
+#ifndef LRS_SWEEP_KEYS_ITEMS
+#define LRS_SWEEP_KEYS_ITEMS 32 // the same for sweeps with no payload phase
+#endif
 #ifndef LRS_SWEEP_BLOCK
 #define LRS_SWEEP_BLOCK 512     // threads per workgroup of the largest sweep tile
 #endif
@@ -57,10 +60,15 @@ enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1, kKeyX32 = 2, kKeyU64 = 3, kKeyX64
 
 // Payload handling of one pass.
 enum PayKind : int {
-    kPayNone = 0,      // keys only
-    kPayU32 = 1,       // read u32, write u32 (pairs; middle passes of the row sort)
-    kPayIdxFirst = 2,  // synthesise the column index, write u32 (first row-sort pass)
-    kPayIdxLast = 3,   // read u32 index, write int64 (last row-sort pass)
+    kPayNone = 0,        // keys only
+    kPayU32 = 1,         // read u32, write u32 (pairs; middle passes of the row sort)
+    kPayIdxFirst = 2,    // synthesise the column index, write u32 (first row-sort pass)
+    kPayIdxLast = 3,     // read u32 index, write int64 (last row-sort pass)
+    // Row sorts of rows of at most 65536 elements carry key and column as one
+    // word, key << 16 | column, between passes (the middle passes are
+    // keys-only sorts of those words by their high half):
+    kPayPackFirst = 4,   // 16-bit patterns in, words out (first pass)
+    kPayUnpackLast = 5,  // words in; the pattern and its int64 column out (last pass)
 };
 
 // ------------------------------------------------------------- key traits
@@ -123,7 +131,24 @@ template <> struct KeyTraits<kKeyX64> {
 template <int KK>
 __device__ inline uint32_t digit_of(typename KeyTraits<KK>::Word v, uint64_t flip, uint64_t flip_neg,
                                     uint32_t shift, uint32_t mask) {
-    return static_cast<uint32_t>(KeyTraits<KK>::key(v, flip, flip_neg) >> shift) & mask;
+    if constexpr (sizeof(typename KeyTraits<KK>::Word) == 8) {
+        return static_cast<uint32_t>(KeyTraits<KK>::key(v, flip, flip_neg) >> shift) & mask;
+    } else {
+        // one bit-field extract (the width is uniform: a scalar popcount)
+        return __builtin_amdgcn_ubfe(KeyTraits<KK>::key(v, flip, flip_neg), shift,
+                                     static_cast<uint32_t>(__builtin_popcount(mask)));
+    }
+}
+
+// Order-preserving key of a 16-bit float pattern and its inverse (negative
+// patterns complemented, non-negative ones with the sign bit set; `flip`
+// complements the key for descending order).
+__device__ inline uint32_t f16_key(uint32_t v, uint32_t flip) {
+    return (v ^ ((v & 0x8000u) ? 0xFFFFu : 0x8000u)) ^ flip;
+}
+__device__ inline uint32_t f16_pattern(uint32_t key, uint32_t flip) {
+    const uint32_t asc = (key ^ flip) & 0xFFFFu;
+    return (asc & 0x8000u) ? (asc ^ 0x8000u) : (~asc & 0xFFFFu);
 }
 
 // Range-checked buffer access: a load past the resource's byte count returns
@@ -270,6 +295,7 @@ __device__ inline W observe(const W *p) {
     return __hip_atomic_load(const_cast<W *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
 // ------------------------------------------------------------ sweep pass
 
 struct SweepArgs {
@@ -316,6 +342,43 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
     return before + inc - v;
 }
 
+// The ITEMS consecutive elements from element `first` of a buffer, into one
+// thread's registers: with 16-, 8- or 4-byte loads when `vec` (every load in
+// range and the buffer's base aligned to the load size), else one load each.
+template <typename Stored, int ITEMS, typename Word>
+__device__ inline void load_run(Word (&key)[ITEMS], __amdgpu_buffer_rsrc_t r, uint32_t first, bool vec) {
+    constexpr uint32_t kBytes = ITEMS * sizeof(Stored);
+    static_assert(sizeof(Stored) <= 4 && sizeof(Word) == 4 && kBytes % 4 == 0, "whole words of 4-byte registers");
+    constexpr uint32_t kVec = kBytes % 16 == 0 ? 16 : kBytes % 8 == 0 ? 8 : 4;
+    if (vec) {
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+        uint32_t w[kBytes / 4];
+        const uint32_t base = first * static_cast<uint32_t>(sizeof(Stored));
+#pragma unroll
+        for (uint32_t q = 0; q < kBytes / kVec; ++q) {
+            const int off = static_cast<int>(base + q * kVec);
+            if constexpr (kVec == 16) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, LRS_LOAD_POLICY);
+                w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+            } else if constexpr (kVec == 8) {
+                const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, LRS_LOAD_POLICY);
+                w[2 * q] = v.x; w[2 * q + 1] = v.y;
+            } else {
+                w[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, LRS_LOAD_POLICY);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            if constexpr (sizeof(Stored) == 4) key[j] = w[j];
+            else key[j] = (w[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(r, first + j);
+    }
+}
+
 // One LSD pass over one tile of BLOCK * ITEMS elements of one row.
 //
 // 1. Load the tile's keys (wave-striped: each wave holds a contiguous run of
@@ -326,6 +389,15 @@ __device__ inline uint32_t block_exclusive_scan_n(uint32_t v, uint32_t *tmp, int
 // 3. Per digit: the tile's count (published at once for the look-back; an
 //    inclusive count for a row's first tile), the digit's start in the tile,
 //    each wave's base inside it, and the row's bucket base.
+//    Narrow digits (at most 4 bits) of sweeps with no payload phase replace
+//    1-3: each thread loads a run of ITEMS consecutive elements, counts its
+//    digits in its own column of LDS counters, and one scan of all counters
+//    in (digit, thread) order gives every element's slot and every digit's
+//    count and start (no ballots: a few instructions per element).
+// 3'. A row-sort pass over 16-bit patterns with the column index as payload
+//    (rows of at most 65536) moves one word per element, key << 16 | column:
+//    the first pass makes the words at load, the middle passes sort them as
+//    plain keys by their high half, the last writes the pattern and column.
 // 4. Move every key to its slot of the tile's digit order in LDS, then walk
 //    the look-back: the digit's count in earlier tiles of the row, read from
 //    the predecessors' published words until an inclusive count is met (or,
@@ -353,7 +425,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
 
     // s_buf holds the tile in digit order (keys, then payload).  Between writing the keys and the payload out of the same slots, each
     // thread keeps its slots' digits in registers, four to a word.
-    __shared__ Word s_buf[TILE];
+    __shared__ __attribute__((aligned(16))) Word s_buf[TILE];
     uint32_t *const s_pay = reinterpret_cast<uint32_t *>(s_buf);  // the payload's view of the slots
     __shared__ uint32_t s_cnt[WAVES][R];      // per-wave digit counts, then per-wave bases
     __shared__ uint32_t s_goff[R];            // output index of digit run start minus local start
@@ -365,6 +437,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     // 64-bit look-back words also mark rows too long for 32-bit buffer offsets
     constexpr bool kWide = sizeof(W) == 8;
+    // Narrow digits of 4-byte words with no separate payload phase rank by
+    // per-thread counting over runs of consecutive elements (a few
+    // instructions per element) instead of by ballots (4 per digit bit).
+    // (Not in partition mode, whose tile loop would need more registers.)
+    constexpr bool kBlocked = B <= 4 && !kWide && !PART && sizeof(Word) == 4 &&
+                              (PK == kPayNone || PK == kPayPackFirst || PK == kPayUnpackLast);
 
     // Each wave clears its own row of counters: only that wave touches it
     // until the barrier after the ranking, and one wave's LDS accesses take
@@ -410,46 +488,142 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
 
         // 1. Keys.  Elements past the end of the row read as 0 and take the
         // largest digit: last in input order, they rank after every real key of
-        // that digit and are never written.
+        // that digit and are never written.  Item j of this thread is tile
+        // element elem(j): wave-striped, or the thread's own run of ITEMS
+        // consecutive elements for the per-thread counting rank.
+        auto elem = [&](int j) -> uint32_t {
+            return kBlocked ? static_cast<uint32_t>(tid) * ITEMS + j : wbase + j * kWave + lane;
+        };
         Word key[ITEMS];
+        if constexpr (kBlocked) {
+            const bool vec = valid == TILE && (reinterpret_cast<uintptr_t>(kin) & 15u) == 0u;
+            load_run<Stored, ITEMS>(key, kin_rsrc, elem(0), vec);
+        } else {
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, wbase + j * kWave + lane);
+            for (int j = 0; j < ITEMS; ++j) key[j] = BufIO<Stored>::load(kin_rsrc, elem(j));
+        }
+        // A first row-sort pass makes the words key << 16 | column at once;
+        // from here on its registers hold u32 words whose digits sit 16 bits up.
+        if constexpr (PK == kPayPackFirst) {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j)
+                key[j] = (f16_key(key[j], static_cast<uint32_t>(a.flip)) << 16) | (tile_start + elem(j));
+        }
         // Digit d's first output index in the row (bucket base), thread d.
         uint32_t bucket_base = 0u;
         if (!PART && tid < static_cast<int>(R))
             bucket_base = a.bases[static_cast<uint64_t>(row) * a.bases_row_stride + tid];
 
-        // 2. Stable rank inside the wave; the group's lowest lane advances the
-        // running count (and clears the mask).
-        uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's digit
-        // Only a row's last tile has elements past the end, so full tiles take a
-        // copy of the loop without the bounds test.
-        auto rank_items = [&](auto partial) {
+        // The pass digit of a key held in registers or LDS.
+        auto reg_digit = [&](Word v) -> uint32_t {
+            if constexpr (PK == kPayPackFirst)
+                return __builtin_amdgcn_ubfe(static_cast<uint32_t>(v), 16u + a.shift,
+                                             static_cast<uint32_t>(__builtin_popcount(a.digit_mask)));
+            else
+                return digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
+        };
+
+        uint32_t rank[ITEMS];  // digit << 16 | rank within the wave's (or thread's) items of the digit
+        uint32_t count = 0u;   // thread d < R: digit d's count in the tile
+        uint32_t local_start = 0u;  // thread d < R: digit d's first slot in the tile
+        if constexpr (kBlocked) {
+            // 2'. Per-thread counting rank (narrow digits): thread t counts its
+            // run's digits in its own column of counters cnt[d][t] (kept in the
+            // tile buffer, which is free until the reorder), and its items of
+            // one digit rank in item order.  The exclusive scan of the counters
+            // in (digit, thread) order is then the first slot of each
+            // (digit, thread) group, which is input order within each digit.
+            uint32_t *cnt = reinterpret_cast<uint32_t *>(s_buf);
+            static_assert(R * BLOCK * sizeof(uint32_t) <= sizeof(s_buf), "the counters fit the tile buffer");
+#pragma unroll
+            for (uint32_t d = 0; d < R; ++d) cnt[d * BLOCK + tid] = 0u;
+            auto count_items = [&](auto partial) {
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) {
+                    const uint32_t dig = reg_digit(key[j]);
+                    const uint32_t d = (decltype(partial)::value && elem(j) >= valid) ? (R - 1u) : dig;
+                    const uint32_t before = cnt[d * BLOCK + tid];
+                    cnt[d * BLOCK + tid] = before + 1u;
+                    rank[j] = (d << 16) | before;
+                }
+            };
+            if (valid == TILE) count_items(std::false_type{});
+            else count_items(std::true_type{});
+            __syncthreads();
+            // Thread t scans counters [t * R, t * R + R) of the (digit, thread)
+            // order: the thread sums of a block scan, then its own run.
+            // (16-byte LDS accesses when the run is whole 16-byte words; the run
+            // is read twice rather than held, which keeps registers for keys)
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            uint32_t sum = 0u;
+            if constexpr (R % 4 == 0) {
+#pragma unroll
+                for (uint32_t i = 0; i < R; i += 4) {
+                    const v4u v = *reinterpret_cast<const v4u *>(cnt + tid * R + i);
+                    sum += v.x + v.y + v.z + v.w;
+                }
+            } else {
+#pragma unroll
+                for (uint32_t i = 0; i < R; ++i) sum += cnt[tid * R + i];
+            }
+            uint32_t run = block_exclusive_scan_n<BLOCK, false>(sum, s_tmp, lane, wave);
+            if constexpr (R % 4 == 0) {
+#pragma unroll
+                for (uint32_t i = 0; i < R; i += 4) {
+                    v4u v = *reinterpret_cast<const v4u *>(cnt + tid * R + i);
+                    const uint32_t e0 = run, e1 = e0 + v.x, e2 = e1 + v.y, e3 = e2 + v.z;
+                    run = e3 + v.w;
+                    *reinterpret_cast<v4u *>(cnt + tid * R + i) = v4u{e0, e1, e2, e3};
+                }
+            } else {
+#pragma unroll
+                for (uint32_t i = 0; i < R; ++i) {
+                    const uint32_t x = cnt[tid * R + i];
+                    cnt[tid * R + i] = run;
+                    run += x;
+                }
+            }
+            __syncthreads();
+            if (tid < static_cast<int>(R)) {
+                local_start = cnt[tid * BLOCK];
+                count = (tid + 1 < static_cast<int>(R) ? cnt[(tid + 1) * BLOCK] : TILE) - local_start;
+            }
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t p = wbase + j * kWave + lane;
-                const uint32_t dig = digit_of<KK>(key[j], a.flip, a.flip_neg, a.shift, a.digit_mask);
-                const uint32_t d = (decltype(partial)::value && p >= valid) ? (R - 1u) : dig;
-                uint32_t below, size;
-                group_rank(match_mask<B>(d), below, size);
-                const uint32_t before = s_cnt[wave][d];
-                rank[j] = (d << 16) | (before + below);
-                pin(rank[j]);
-                if (below == 0u) s_cnt[wave][d] = before + size;
+                const uint32_t d = rank[j] >> 16;
+                rank[j] = cnt[d * BLOCK + tid] + (rank[j] & 0xFFFFu);
             }
-        };
-        if (valid == TILE) rank_items(std::false_type{});
-        else rank_items(std::true_type{});
-        __syncthreads();
-
-        // 3. Digit d is owned by thread d.
-        uint32_t count = 0u;
-        if (tid < static_cast<int>(R)) {
+            __syncthreads();  // every counter read before the tile overwrites them
+        } else {
+            // 2. Stable rank inside the wave; the group's lowest lane advances the
+            // running count (and clears the mask).
+            // Only a row's last tile has elements past the end, so full tiles take a
+            // copy of the loop without the bounds test.
+            auto rank_items = [&](auto partial) {
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                const uint32_t c = s_cnt[w][tid];
-                s_cnt[w][tid] = count;
-                count += c;
+                for (int j = 0; j < ITEMS; ++j) {
+                    const uint32_t dig = reg_digit(key[j]);
+                    const uint32_t d = (decltype(partial)::value && elem(j) >= valid) ? (R - 1u) : dig;
+                    uint32_t below, size;
+                    group_rank(match_mask<B>(d), below, size);
+                    const uint32_t before = s_cnt[wave][d];
+                    rank[j] = (d << 16) | (before + below);
+                    pin(rank[j]);
+                    if (below == 0u) s_cnt[wave][d] = before + size;
+                }
+            };
+            if (valid == TILE) rank_items(std::false_type{});
+            else rank_items(std::true_type{});
+            __syncthreads();
+
+            // 3. Digit d is owned by thread d.
+            if (tid < static_cast<int>(R)) {
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) {
+                    const uint32_t c = s_cnt[w][tid];
+                    s_cnt[w][tid] = count;
+                    count += c;
+                }
             }
         }
         uint32_t real = count;  // padding is not part of the count of the last digit
@@ -458,25 +632,28 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
         if (!PART && tid < static_cast<int>(R))
             publish(status + tid, static_cast<W>((tile_in_row == 0 ? St::kInclusive : St::kAggregate) |
                                                  static_cast<W>(real)));
-        // (s_tmp is written again only by the next tile, after three barriers)
-        const uint32_t local_start = block_exclusive_scan_n<BLOCK, false>(count, s_tmp, lane, wave);
-        if (tid < static_cast<int>(R)) {
+        if constexpr (!kBlocked) {
+            // (s_tmp is written again only by the next tile, after three barriers)
+            local_start = block_exclusive_scan_n<BLOCK, false>(count, s_tmp, lane, wave);
+            if (tid < static_cast<int>(R)) {
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
-        }
-        __syncthreads();
+                for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
+            }
+            __syncthreads();
 
-        // 4. Local reorder.
+            // 4. Local reorder: every key to its slot.
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t d = rank[j] >> 16;
-            const uint32_t slot = s_cnt[wave][d] + (rank[j] & 0xFFFFu);
-            s_buf[slot] = key[j];
-            rank[j] = slot;
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t d = rank[j] >> 16;
+                const uint32_t slot = s_cnt[wave][d] + (rank[j] & 0xFFFFu);
+                s_buf[slot] = key[j];
+                rank[j] = slot;
+            }
+        } else {
+            // 4. Local reorder: every key to its slot.
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) s_buf[rank[j]] = key[j];
         }
-
-
-
         // Look-back walk, one thread per digit.  Each round trip a lane reads its
         // digit's words of the next kLookback predecessors (nearest first) and adds
         // counts until an inclusive count or an unpublished word.  Lanes of a wave
@@ -502,14 +679,14 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             uint32_t polls = 0;
             uint32_t back = 1;  // the next predecessor to consume is tile t - back
             const W *row_status = static_cast<const W *>(a.status) + tid;
+            auto status_of = [&](uint32_t tp) -> W { return observe(row_status + static_cast<uint64_t>(tp) * R); };
             for (;;) {
                 const uint64_t walking = __builtin_amdgcn_ballot_w64(!done);
                 if (walking == 0 || gave_up) break;
                 W sv[kLookback];
 #pragma unroll
                 for (int i = 0; i < kLookback; ++i)
-                    sv[i] = (!done && back + i <= tile_in_row)
-                        ? observe(row_status + static_cast<uint64_t>(t - back - i) * R) : W(0);
+                    sv[i] = (!done && back + i <= tile_in_row) ? status_of(t - back - i) : W(0);
                 uint32_t used = 0;
 #pragma unroll
                 for (int i = 0; i < kLookback; ++i) {
@@ -522,7 +699,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                 back += used;
                 if (__builtin_amdgcn_ballot_w64(used != 0) == 0) {
                     const int leader = __builtin_ctzll(walking);
-                    const W *word = row_status + static_cast<uint64_t>(t - back) * R;
                     for (;;) {
                         if (++polls > a.spin_limit) {
                             gave_up = true;
@@ -530,7 +706,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                         }
                         __builtin_amdgcn_s_sleep(2);
                         W pv = 0;
-                        if (lane == leader) pv = observe(word);
+                        if (lane == leader) pv = status_of(t - back);
                         if (__builtin_amdgcn_ballot_w64(lane == leader && (pv & ~St::kMask) != 0) != 0) break;
                     }
                 }
@@ -567,11 +743,22 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
         // 5. Keys out: slot k goes to s_goff[d] + k.  That is below row_len for
         // every real element; the range check of the buffer store only keeps a
         // logic error from becoming a stray store.
+        constexpr bool kPayPhase = PK == kPayU32 || PK == kPayIdxFirst || PK == kPayIdxLast;
+        constexpr bool kWords = PK == kPayPackFirst || PK == kPayUnpackLast;
+        static_assert(!kWords || !kWide, "rows of packed words are short");
         Stored *kout = static_cast<Stored *>(a.keys_out) + row_base;
         uint32_t slot_digits[(ITEMS + 3) / 4];
 #pragma unroll
         for (int i = 0; i < (ITEMS + 3) / 4; ++i) slot_digits[i] = 0u;
-        const __amdgpu_buffer_rsrc_t kout_rsrc = make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
+        // the key outputs: patterns or words as read, packed words (first
+        // pass), or the pattern and the int64 column (last pass)
+        const __amdgpu_buffer_rsrc_t kout_rsrc =
+            PK == kPayPackFirst  ? make_rsrc(static_cast<uint32_t *>(a.keys_out) + row_base, a.row_len * 4u)
+            : PK == kPayUnpackLast ? make_rsrc(static_cast<uint16_t *>(a.keys_out) + row_base, a.row_len * 2u)
+                                   : make_rsrc(kout, kWide ? 0u : a.row_len * sizeof(Stored));
+        const __amdgpu_buffer_rsrc_t iout_rsrc =
+            make_rsrc(static_cast<int64_t *>(a.vals_out) + (PK == kPayUnpackLast ? row_base : 0u),
+                      PK == kPayUnpackLast ? a.row_len * 8u : 0u);
         // Without the bounds select (full tiles) the loop has no branches and
         // all of a thread's slot reads can be in flight at once.
         auto keys_out = [&](auto partial) {
@@ -579,12 +766,18 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             for (int i = 0; i < ITEMS; ++i) {
                 const uint32_t k = i * BLOCK + tid;
                 const Word v = s_buf[k];
-                const uint32_t d = digit_of<KK>(v, a.flip, a.flip_neg, a.shift, a.digit_mask);
-                if constexpr (PK != kPayNone) slot_digits[i / 4] |= d << (8 * (i % 4));
+                const uint32_t d = reg_digit(v);
+                if constexpr (kPayPhase) slot_digits[i / 4] |= d << (8 * (i % 4));
                 uint32_t dst;
                 if constexpr (decltype(partial)::value) dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
                 else dst = s_goff[d] + k;
-                if constexpr (kWide) {
+                if constexpr (PK == kPayPackFirst) {
+                    BufIO<uint32_t>::store(kout_rsrc, dst, static_cast<uint32_t>(v));
+                } else if constexpr (PK == kPayUnpackLast) {
+                    BufIO<uint16_t>::store(kout_rsrc, dst, f16_pattern(static_cast<uint32_t>(v) >> 16,
+                                                                       static_cast<uint32_t>(a.flip)));
+                    BufIO<int64_t>::store(iout_rsrc, dst, static_cast<uint32_t>(v) & 0xFFFFu);
+                } else if constexpr (kWide) {
                     if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
                 } else {
                     BufIO<Stored>::store(kout_rsrc, dst, v);
@@ -605,7 +798,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
         }
 
-        if constexpr (PK != kPayNone) {
+        if constexpr (kPayPhase) {
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
@@ -794,17 +987,6 @@ struct RowResidentArgs {
     uint32_t flip;             // 0xFFFF: descending
 };
 
-// Order-preserving key of a 16-bit float pattern and its inverse (negative
-// patterns complemented, non-negative ones with the sign bit set; `flip`
-// complements the key for descending order).
-__device__ inline uint32_t f16_key(uint32_t v, uint32_t flip) {
-    return (v ^ ((v & 0x8000u) ? 0xFFFFu : 0x8000u)) ^ flip;
-}
-__device__ inline uint32_t f16_pattern(uint32_t key, uint32_t flip) {
-    const uint32_t asc = (key ^ flip) & 0xFFFFu;
-    return (asc & 0x8000u) ? (asc ^ 0x8000u) : (~asc & 0xFFFFu);
-}
-
 // Sorts whole rows of 16-bit float patterns inside LDS, all passes of the
 // 16-bit key, one row at a time per workgroup (workgroups loop over rows).
 //
@@ -972,12 +1154,15 @@ constexpr int kHistBlock = LRS_HIST_BLOCK;  // threads per histogram workgroup
 
 // Counts every pass's digit over one share of one row in LDS, from one read of
 // the keys with 16-byte loads, then adds the counts to the row's histogram.
+// Digits narrower than 8 bits are counted per byte of the key window (one LDS
+// add per byte instead of one per pass: LDS adds bound this kernel) and each
+// pass's counts are folded from its byte's counts at the end.
 // Lane l counts into copy l % kHistCopies of the counters, and the copies of
 // one counter sit in consecutive words: with 32 copies a lane's LDS bank
 // depends on its lane alone, whatever the digits, and lanes that share a
-// digit do not serialise on one address (except lanes l and l + 32).  The pass loop
-// is unrolled: each pass costs one bit-field extract, one address add and one
-// LDS add whose pass offset is an immediate.
+// digit do not serialise on one address (except lanes l and l + 32).  The
+// counting loop is unrolled: each digit costs one bit-field extract, one
+// address add and one LDS add whose offset is an immediate.
 template <int B, int KK>
 __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t R = 1u << B;
@@ -986,26 +1171,34 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
     constexpr uint32_t kPerVec = 16u / sizeof(Stored);
     constexpr int kMaxPasses = (8 * static_cast<int>(sizeof(Stored)) + B - 1) / B;
     static_assert(kMaxPasses * R <= kHistMaxCounters, "counters must fit");
+    // counted digits: the passes' own (8-bit digits) or whole bytes of the window
+    constexpr bool kBytes = B < 8;
+    constexpr uint32_t kCB = kBytes ? 8u : static_cast<uint32_t>(B);  // counted digit width
+    constexpr uint32_t kCR = 1u << kCB;
+    constexpr int kMaxCounted = kBytes ? static_cast<int>(sizeof(Stored)) : kMaxPasses;
     // half the copies when the counters would not fit in 128 KB (8-bit digits of 64-bit keys)
-    constexpr int kCopies = (kMaxPasses * R * kHistCopies * 4 <= 131072) ? kHistCopies : kHistCopies / 2;
-    constexpr uint32_t kPassWords = R * kCopies;
+    constexpr int kCopies = (kMaxCounted * kCR * kHistCopies * 4 <= 131072) ? kHistCopies : kHistCopies / 2;
+    constexpr uint32_t kPassWords = kCR * kCopies;
     constexpr int kUnroll = 4;
-    __shared__ uint32_t s_h[kMaxPasses * R * kCopies];  // 128 KB for 8-bit digits of u32 keys
+    __shared__ uint32_t s_h[kMaxCounted * kCR * kCopies];  // 128 KB for u32 keys
+    // byte counts summed over the copies, from which the passes' counts fold
+    __shared__ uint32_t s_byte[kBytes ? kMaxCounted * kCR : 1];
 
     const uint32_t row = blockIdx.x / a.chunks_per_row;
     const uint32_t chunk = blockIdx.x - row * a.chunks_per_row;
     const uint32_t total = a.passes * R;
-    for (uint32_t i = threadIdx.x; i < total * kCopies; i += kHistBlock) s_h[i] = 0u;
+    const uint32_t counted = kBytes ? (a.end_bit - a.begin_bit + 7u) / 8u : a.passes;
+    for (uint32_t i = threadIdx.x; i < counted * kPassWords; i += kHistBlock) s_h[i] = 0u;
     __syncthreads();
 
     uint32_t *mine = s_h + (threadIdx.x % kCopies);
     auto count_key = [&](Word v) {
         const Word k = KeyTraits<KK>::key(v, a.flip, a.flip_neg);
 #pragma unroll
-        for (int p = 0; p < kMaxPasses; ++p) {
-            if (p < static_cast<int>(a.passes)) {
-                const uint32_t shift = a.begin_bit + static_cast<uint32_t>(p) * B;
-                const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
+        for (int p = 0; p < kMaxCounted; ++p) {
+            if (p < static_cast<int>(counted)) {
+                const uint32_t shift = a.begin_bit + static_cast<uint32_t>(p) * kCB;
+                const uint32_t width = min(kCB, a.end_bit - shift);
                 uint32_t d;
                 if constexpr (sizeof(Word) == 8) d = static_cast<uint32_t>(k >> shift) & ((1u << width) - 1u);
                 else d = __builtin_amdgcn_ubfe(k, shift, width);
@@ -1059,15 +1252,41 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
         count_key(static_cast<Word>(base[body_end + threadIdx.x]));
     __syncthreads();
 
-    // this workgroup's count of counter i (copies taken in a rotated order so
-    // neighbouring threads read different banks)
-    auto lds_count = [&](uint32_t i) {
-        const uint32_t p = i / R, d = i - p * R;
+    // this workgroup's count of counted digit i (copies taken in a rotated
+    // order so neighbouring threads read different banks)
+    auto copies_sum = [&](uint32_t i) {
+        const uint32_t p = i / kCR, d = i - p * kCR;
         uint32_t c = 0;
 #pragma unroll
         for (int k = 0; k < kCopies; ++k)
             c += s_h[p * kPassWords + d * kCopies + ((k + i) % kCopies)];
         return c;
+    };
+    if constexpr (kBytes) {
+        for (uint32_t i = threadIdx.x; i < counted * kCR; i += kHistBlock) s_byte[i] = copies_sum(i);
+        __syncthreads();
+    }
+    // this workgroup's count of digit d of pass p (i = p * R + d): with byte
+    // counts, the sum over the byte values whose bits at the pass's offset in
+    // its byte are d (the other bits of the byte run over every value)
+    auto lds_count = [&](uint32_t i) -> uint32_t {
+        if constexpr (!kBytes) {
+            return copies_sum(i);
+        } else {
+            const uint32_t p = i / R, d = i - p * R;
+            const uint32_t byte = p / (8u / B), off = (p % (8u / B)) * B;
+            const uint32_t shift = a.begin_bit + p * B;
+            const uint32_t width = min(static_cast<uint32_t>(B), a.end_bit - shift);
+            const uint32_t byte_width = min(8u, a.end_bit - (a.begin_bit + byte * 8u));
+            const uint32_t free_bits = byte_width - width;
+            const uint32_t low_mask = (1u << off) - 1u;
+            uint32_t c = 0;
+            for (uint32_t t = 0; t < (1u << free_bits); ++t) {
+                const uint32_t v = (t & low_mask) | (d << off) | ((t >> off) << (off + width));
+                c += s_byte[byte * kCR + v];
+            }
+            return c;
+        }
     };
     uint32_t *out = a.hist + static_cast<uint64_t>(row) * total;
     for (uint32_t i = threadIdx.x; i < total; i += kHistBlock) {

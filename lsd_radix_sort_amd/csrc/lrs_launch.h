@@ -23,9 +23,18 @@ struct TileCfg {
 };
 constexpr TileCfg kTileCfgs[3] = {
     {256, 16, 4096}, {512, 16, 8192}, {kSweepBlock, LRS_SWEEP_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_ITEMS}};
+// Sweeps of 4-byte words with no payload phase (keys only, and the row-sort
+// passes over packed key/column words) hold fewer registers per element: a
+// larger largest tile (rows of 65536 then take four tiles instead of eight).
+constexpr TileCfg kTileCfgsKeys[3] = {
+    {256, 16, 4096}, {512, 16, 8192},
+    {kSweepBlock, LRS_SWEEP_KEYS_ITEMS, uint64_t(kSweepBlock) * LRS_SWEEP_KEYS_ITEMS}};
 // 64-bit keys take twice the registers and LDS per key: half the keys per tile.
 constexpr TileCfg kTileCfgs64[3] = {{256, 8, 2048}, {512, 8, 4096}, {512, 16, 8192}};
-constexpr TileCfg tile_cfg_of(bool key64, int c) { return key64 ? kTileCfgs64[c] : kTileCfgs[c]; }
+constexpr bool no_payload_phase(int pk) { return pk == kPayNone || pk == kPayPackFirst || pk == kPayUnpackLast; }
+constexpr TileCfg tile_cfg_of(bool key64, int c, bool keys_only) {
+    return key64 ? kTileCfgs64[c] : keys_only ? kTileCfgsKeys[c] : kTileCfgs[c];
+}
 
 // One LSD pass: `grid` workgroups (one per tile, or one per partition with
 // PART), tile shape `cfg`, 64-bit look-back words and store addresses when

@@ -22,13 +22,16 @@ void launch_sweep_cfg(const SweepArgs &a, uint64_t grid_size, hipStream_t s) {
 template <int B, int KK, int PK, bool PART>
 hipError_t launch_sweep_b(const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s) {
     constexpr bool k64 = sizeof(typename KeyTraits<KK>::Stored) == 8;
-    constexpr TileCfg c0 = tile_cfg_of(k64, 0), c1 = tile_cfg_of(k64, 1), c2 = tile_cfg_of(k64, 2);
+    constexpr bool ko = no_payload_phase(PK);
+    constexpr TileCfg c0 = tile_cfg_of(k64, 0, ko), c1 = tile_cfg_of(k64, 1, ko), c2 = tile_cfg_of(k64, 2, ko);
     // 64-bit look-back words (and 64-bit store addressing) only occur for rows
     // of 2^29 or more elements (2^30 for 4-byte keys), which always take the
-    // largest tile.
-    if (wide)
-        launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint64_t, PART>(a, grid, s);
-    else if (cfg == 2)
+    // largest tile; rows carried as packed words are at most 65536 long.
+    constexpr bool kPacked = PK == kPayPackFirst || PK == kPayUnpackLast;
+    if (wide) {
+        if constexpr (kPacked) return hipErrorInvalidValue;
+        else launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint64_t, PART>(a, grid, s);
+    } else if (cfg == 2)
         launch_sweep_cfg<B, c2.items, c2.block, KK, PK, uint32_t, PART>(a, grid, s);
     else if (cfg == 1)
         launch_sweep_cfg<B, c1.items, c1.block, KK, PK, uint32_t, PART>(a, grid, s);

@@ -35,9 +35,13 @@ def test_wide_key_sweep_bytes():
 
 
 def test_row_sort_bytes():
-    # fp16 rows, 4 passes: 2 in + 2+4 out, then 6 + 6 twice, then 6 in + 2+8 out = 48 B per element
+    # fp16 rows of 65536, 4 passes, key << 16 | column as one u32 word between
+    # passes: 2 in + 4 out, then 4 + 4 twice, then 4 in + 2+8 out = 36 B per element
     w = bench.WORKLOADS["c4_fp16_1024x65536_asc"]
-    assert bench.sweep_bytes(w) == 48 * 1024 * 65536
+    assert bench.sweep_bytes(w) == 36 * 1024 * 65536
+    # longer rows keep the pattern and a u32 index apart: 2 in + 2+4 out, then
+    # 6 + 6 twice, then 6 in + 2+8 out = 48 B per element
+    assert bench.sweep_bytes(dict(w, rows=1, cols=200_000)) == 48 * 200_000
     # whole-row sort: the pattern in, the pattern and an int64 index out
     assert bench.resident_bytes(bench.WORKLOADS["c5_bf16_4096x4096_desc"]) == 12 * 4096 * 4096
     assert bench.resident_bytes(bench.WORKLOADS["c1_keys_1k_4bit"]) == 8 * 1024

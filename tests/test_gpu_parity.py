@@ -150,6 +150,33 @@ def test_exact_tile_multiples(n):
     assert_same(to_np_u32(gi), ei, "int32 keys only")
 
 
+@pytest.mark.parametrize("b", [4, 8])
+def test_keys_at_unaligned_addresses(b):
+    """Keys and rows that start off a 16-byte boundary: the per-thread runs of
+    narrow-digit sweeps are then read one element at a time, not as vectors."""
+    n = 3_000_017
+    keys = workloads.random_u32(4800 + b, n + 3)
+    base = to_gpu(keys)
+    for off in (1, 2, 3):
+        log(f"unaligned keys offset={off} b={b}")
+        kt = base[off:]
+        assert kt.data_ptr() % 16 != 0
+        out = lrs.radix_sort_keys(kt, 0, 32, b)
+        torch.cuda.synchronize()
+        assert_same(to_np_u32(out), oracle.radix_sort_keys(keys[off:], 0, 32, b), f"offset {off}")
+    rows, m = 3, 40_000
+    bits = workloads.fp16_normal_bits(4900 + b, rows * m + 5)
+    t = to_gpu(bits).view(torch.float16)
+    for off in (1, 3, 5):
+        x = t[off:off + rows * m].view(rows, m)
+        assert x.data_ptr() % 16 != 0
+        ev, ei = oracle.segmented_row_sort(bits[off:off + rows * m].reshape(rows, m), False, b)
+        vo, io = lrs.segmented_row_sort(x, False, b)
+        torch.cuda.synchronize()
+        assert_same(vo.view(torch.int16).cpu().numpy().view(np.uint16).ravel(), ev.ravel(), f"rows offset {off}")
+        assert_same(io.cpu().numpy().ravel(), ei.ravel(), f"rows offset {off} idx")
+
+
 def test_pass_by_pass_states():
     # the state after p passes is the stable sort by the low p*b bits of the window
     n = 300_001
@@ -215,7 +242,7 @@ def test_empty_input():
 def test_digit_histograms():
     keys = workloads.pairs_c3(1 << 20, "and3")[0]
     kt = to_gpu(keys)
-    for begin, end, b in ((0, 32, 8), (0, 32, 4), (0, 12, 4), (3, 30, 1), (5, 17, 2)):
+    for begin, end, b in ((0, 32, 8), (0, 32, 4), (0, 12, 4), (3, 30, 1), (5, 17, 2), (1, 30, 4), (7, 32, 2)):
         h = lrs.radix_sort_digit_histograms(kt, begin, end, b)
         torch.cuda.synchronize()
         exp = oracle.all_pass_histograms(keys, begin, end, b)
@@ -351,7 +378,7 @@ def test_c5_bf16_4096x4096_descending():
 
 
 @pytest.mark.parametrize("rows,n", [(1, 1), (3, 7), (5, 4095), (2, 4097), (3, 8192), (3, 8193), (7, 12345),
-                                     (1, 70000), (300, 33), (2, 200_000)])
+                                     (3, 65535), (2, 65536), (2, 65537), (1, 70000), (300, 33), (2, 200_000)])
 @pytest.mark.parametrize("b", [1, 2, 4, 8])
 def test_rows_ragged_shapes(rows, n, b):
     bits = workloads.fp16_normal_bits(rows * 131 + n, rows * n).reshape(rows, n)
