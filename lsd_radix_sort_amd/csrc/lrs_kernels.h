@@ -379,6 +379,81 @@ __device__ inline void load_run(Word (&key)[ITEMS], __amdgpu_buffer_rsrc_t r, ui
     }
 }
 
+// Per-thread counting rank of one tile (digits of at most 4 bits).  Thread t
+// holds the tile's elements t * ITEMS .. t * ITEMS + ITEMS - 1 and counts
+// their digits (dig(j), padding already mapped to the last digit) in its own
+// column of counters cnt[d * BLOCK + t] (R * BLOCK words of LDS); its items of
+// one digit rank in item order.  rank[j] = digit << 16 | rank among the
+// thread's items of that digit.
+template <uint32_t R, int ITEMS, int BLOCK, typename Dig>
+__device__ inline void thread_count_digits(Dig dig, uint32_t (&rank)[ITEMS], uint32_t *cnt, int tid) {
+#pragma unroll
+    for (uint32_t d = 0; d < R; ++d) cnt[d * BLOCK + tid] = 0u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t d = dig(j);
+        const uint32_t before = cnt[d * BLOCK + tid];
+        cnt[d * BLOCK + tid] = before + 1u;
+        rank[j] = (d << 16) | before;
+    }
+}
+
+// The exclusive scan of those counters in (digit, thread) order is the first
+// slot of each (digit, thread) group of the tile's digit order, which is
+// input order within each digit.  Turns rank[j] into item j's slot, and gives
+// thread d < R its digit's count and first slot.  Starts and ends with a
+// barrier; after it the counters' LDS is free.
+template <uint32_t R, int ITEMS, int BLOCK>
+__device__ inline void thread_counts_to_slots(uint32_t (&rank)[ITEMS], uint32_t *cnt, uint32_t *s_tmp, int tid,
+                                              int lane, int wave, uint32_t &count, uint32_t &local_start) {
+    constexpr uint32_t TILE = static_cast<uint32_t>(BLOCK) * ITEMS;
+    __syncthreads();
+    // Thread t scans counters [t * R, t * R + R): the thread sums go through
+    // a block scan, then the thread's own run.  (16-byte LDS accesses when the
+    // run is whole 16-byte words; the run is read twice rather than held,
+    // which keeps registers for the keys.)
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    uint32_t sum = 0u;
+    if constexpr (R % 4 == 0) {
+#pragma unroll
+        for (uint32_t i = 0; i < R; i += 4) {
+            const v4u v = *reinterpret_cast<const v4u *>(cnt + tid * R + i);
+            sum += v.x + v.y + v.z + v.w;
+        }
+    } else {
+#pragma unroll
+        for (uint32_t i = 0; i < R; ++i) sum += cnt[tid * R + i];
+    }
+    uint32_t run = block_exclusive_scan_n<BLOCK, false>(sum, s_tmp, lane, wave);
+    if constexpr (R % 4 == 0) {
+#pragma unroll
+        for (uint32_t i = 0; i < R; i += 4) {
+            const v4u v = *reinterpret_cast<const v4u *>(cnt + tid * R + i);
+            const uint32_t e0 = run, e1 = e0 + v.x, e2 = e1 + v.y, e3 = e2 + v.z;
+            run = e3 + v.w;
+            *reinterpret_cast<v4u *>(cnt + tid * R + i) = v4u{e0, e1, e2, e3};
+        }
+    } else {
+#pragma unroll
+        for (uint32_t i = 0; i < R; ++i) {
+            const uint32_t x = cnt[tid * R + i];
+            cnt[tid * R + i] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    if (tid < static_cast<int>(R)) {
+        local_start = cnt[tid * BLOCK];
+        count = (tid + 1 < static_cast<int>(R) ? cnt[(tid + 1) * BLOCK] : TILE) - local_start;
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t d = rank[j] >> 16;
+        rank[j] = cnt[d * BLOCK + tid] + (rank[j] & 0xFFFFu);
+    }
+    __syncthreads();  // every counter read before the caller reuses the LDS
+}
+
 // One LSD pass over one tile of BLOCK * ITEMS elements of one row.
 //
 // 1. Load the tile's keys (wave-striped: each wave holds a contiguous run of
@@ -527,73 +602,16 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
         uint32_t count = 0u;   // thread d < R: digit d's count in the tile
         uint32_t local_start = 0u;  // thread d < R: digit d's first slot in the tile
         if constexpr (kBlocked) {
-            // 2'. Per-thread counting rank (narrow digits): thread t counts its
-            // run's digits in its own column of counters cnt[d][t] (kept in the
-            // tile buffer, which is free until the reorder), and its items of
-            // one digit rank in item order.  The exclusive scan of the counters
-            // in (digit, thread) order is then the first slot of each
-            // (digit, thread) group, which is input order within each digit.
+            // 2'. Per-thread counting rank (narrow digits), over the tile
+            // buffer, which is free until the reorder.
             uint32_t *cnt = reinterpret_cast<uint32_t *>(s_buf);
             static_assert(R * BLOCK * sizeof(uint32_t) <= sizeof(s_buf), "the counters fit the tile buffer");
-#pragma unroll
-            for (uint32_t d = 0; d < R; ++d) cnt[d * BLOCK + tid] = 0u;
-            auto count_items = [&](auto partial) {
-#pragma unroll
-                for (int j = 0; j < ITEMS; ++j) {
-                    const uint32_t dig = reg_digit(key[j]);
-                    const uint32_t d = (decltype(partial)::value && elem(j) >= valid) ? (R - 1u) : dig;
-                    const uint32_t before = cnt[d * BLOCK + tid];
-                    cnt[d * BLOCK + tid] = before + 1u;
-                    rank[j] = (d << 16) | before;
-                }
-            };
-            if (valid == TILE) count_items(std::false_type{});
-            else count_items(std::true_type{});
-            __syncthreads();
-            // Thread t scans counters [t * R, t * R + R) of the (digit, thread)
-            // order: the thread sums of a block scan, then its own run.
-            // (16-byte LDS accesses when the run is whole 16-byte words; the run
-            // is read twice rather than held, which keeps registers for keys)
-            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-            uint32_t sum = 0u;
-            if constexpr (R % 4 == 0) {
-#pragma unroll
-                for (uint32_t i = 0; i < R; i += 4) {
-                    const v4u v = *reinterpret_cast<const v4u *>(cnt + tid * R + i);
-                    sum += v.x + v.y + v.z + v.w;
-                }
-            } else {
-#pragma unroll
-                for (uint32_t i = 0; i < R; ++i) sum += cnt[tid * R + i];
-            }
-            uint32_t run = block_exclusive_scan_n<BLOCK, false>(sum, s_tmp, lane, wave);
-            if constexpr (R % 4 == 0) {
-#pragma unroll
-                for (uint32_t i = 0; i < R; i += 4) {
-                    v4u v = *reinterpret_cast<const v4u *>(cnt + tid * R + i);
-                    const uint32_t e0 = run, e1 = e0 + v.x, e2 = e1 + v.y, e3 = e2 + v.z;
-                    run = e3 + v.w;
-                    *reinterpret_cast<v4u *>(cnt + tid * R + i) = v4u{e0, e1, e2, e3};
-                }
-            } else {
-#pragma unroll
-                for (uint32_t i = 0; i < R; ++i) {
-                    const uint32_t x = cnt[tid * R + i];
-                    cnt[tid * R + i] = run;
-                    run += x;
-                }
-            }
-            __syncthreads();
-            if (tid < static_cast<int>(R)) {
-                local_start = cnt[tid * BLOCK];
-                count = (tid + 1 < static_cast<int>(R) ? cnt[(tid + 1) * BLOCK] : TILE) - local_start;
-            }
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t d = rank[j] >> 16;
-                rank[j] = cnt[d * BLOCK + tid] + (rank[j] & 0xFFFFu);
-            }
-            __syncthreads();  // every counter read before the tile overwrites them
+            if (valid == TILE)
+                thread_count_digits<R, ITEMS, BLOCK>([&](int j) { return reg_digit(key[j]); }, rank, cnt, tid);
+            else
+                thread_count_digits<R, ITEMS, BLOCK>(
+                    [&](int j) { return elem(j) >= valid ? R - 1u : reg_digit(key[j]); }, rank, cnt, tid);
+            thread_counts_to_slots<R, ITEMS, BLOCK>(rank, cnt, s_tmp, tid, lane, wave, count, local_start);
         } else {
             // 2. Stable rank inside the wave; the group's lowest lane advances the
             // running count (and clears the mask).
