@@ -366,6 +366,10 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     h.flip = flip;
     h.flip_neg = flip_neg;
     h.atomic = accumulate ? 1u : 0u;
+    if (!accumulate && ws != nullptr) {
+        h.status0 = reinterpret_cast<uint32_t *>(ws + p.off_status[0]);
+        h.status0_row_words = static_cast<uint32_t>(p.status_bytes / 4 / p.rows);
+    }
     const uint32_t blocks = static_cast<uint32_t>(p.rows * p.hist_chunks_per_row);
     TimedLaunch t(1, c);
     hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, blocks, c.s)
@@ -424,6 +428,19 @@ bool key_transform(int key_type, int descending, int &kk, uint64_t &flip, uint64
 
 bool key_type_is_64(int key_type) {
     return key_type == LRS_KEY_U64 || key_type == LRS_KEY_I64 || key_type == LRS_KEY_F64;
+}
+
+// Every pass's digit counts and bucket bases, before the first pass.  With
+// several histogram workgroups per row their counts meet in global atomics,
+// so the histogram, the finished-workgroup counters and the first pass's
+// look-back words are cleared by a launch of their own first; with one per
+// row the histogram kernel stores the counts and clears the row's first-pass
+// look-back words itself (one launch fewer).
+hipError_t launch_counts(const Plan &p, const void *keys, uint32_t *hist, int kk, uint64_t flip, uint64_t flip_neg,
+                         uint8_t *ws, const Ctx &c) {
+    const bool accumulate = p.hist_chunks_per_row > 1;
+    if (accumulate && launch_clear(p, ws, true, c) != hipSuccess) return hipErrorLaunchFailure;
+    return launch_histogram(p, keys, hist, kk, flip, flip_neg, accumulate, ws, c);
 }
 
 // Reduce-then-scan passes (CUDA Handbook ch.16: count, scan the counts, scatter;
@@ -535,9 +552,7 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
     if (c.scan == LRS_SCAN_REDUCE_THEN_SCAN)
         return sort_32_reduce_then_scan(p, kk, flip, flip_neg, pairs, keys_in, vals_in, keys_out, vals_out, ws, c);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, ws, c) != hipSuccess)
-        return LRS_ERR_HIP;
+    if (launch_counts(p, keys_in, hist, kk, flip, flip_neg, ws, c) != hipSuccess) return LRS_ERR_HIP;
 
     uint32_t *alt_k = reinterpret_cast<uint32_t *>(ws + p.off_alt_keys);
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
@@ -597,9 +612,7 @@ int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, keys_in, hist, kk, flip, flip_neg, p.hist_chunks_per_row > 1, ws, c) != hipSuccess)
-        return LRS_ERR_HIP;
+    if (launch_counts(p, keys_in, hist, kk, flip, flip_neg, ws, c) != hipSuccess) return LRS_ERR_HIP;
     uint64_t *alt_k = reinterpret_cast<uint64_t *>(ws + p.off_alt_keys);
     uint32_t *alt_v = reinterpret_cast<uint32_t *>(ws + p.off_alt_vals);
     const uint64_t *src_k = keys_in;
@@ -687,9 +700,7 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + p.off_hist);
-    if (launch_clear(p, ws, p.hist_chunks_per_row > 1, c) != hipSuccess) return LRS_ERR_HIP;
-    if (launch_histogram(p, vals_in, hist, kKeyF16, flip, 0, p.hist_chunks_per_row > 1, ws, c) != hipSuccess)
-        return LRS_ERR_HIP;
+    if (launch_counts(p, vals_in, hist, kKeyF16, flip, 0, ws, c) != hipSuccess) return LRS_ERR_HIP;
 
     uint16_t *alt_k = reinterpret_cast<uint16_t *>(ws + p.off_alt_keys);
     uint32_t *idx[2] = {reinterpret_cast<uint32_t *>(ws + p.off_idx[0]),

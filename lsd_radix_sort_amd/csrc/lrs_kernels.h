@@ -614,7 +614,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             thread_counts_to_slots<R, ITEMS, BLOCK>(rank, cnt, s_tmp, tid, lane, wave, count, local_start);
         } else {
             // 2. Stable rank inside the wave; the group's lowest lane advances the
-            // running count (and clears the mask).
+            // wave's running count of the digit.
             // Only a row's last tile has elements past the end, so full tiles take a
             // copy of the loop without the bounds test.
             auto rank_items = [&](auto partial) {
@@ -1158,6 +1158,8 @@ struct HistArgs {
     uint32_t atomic;         // 1: several workgroups per row accumulate; 0: one writes it
     uint32_t *bases;         // [rows][passes][R] bucket bases written by the row's last workgroup, or NULL
     uint32_t *done;          // [rows] workgroups finished per row, zero on entry (atomic only)
+    uint32_t *status0;       // one workgroup per row: the first pass's look-back words, cleared here (or NULL)
+    uint32_t status0_row_words;  // 32-bit words of them per row
 };
 
 constexpr int kHistMaxCounters = 2048;  // passes * R for every legal (window, b, key width)
@@ -1205,6 +1207,10 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
     const uint32_t row = blockIdx.x / a.chunks_per_row;
     const uint32_t chunk = blockIdx.x - row * a.chunks_per_row;
     const uint32_t total = a.passes * R;
+    if (!a.atomic && a.status0 != nullptr) {
+        uint32_t *st = a.status0 + static_cast<uint64_t>(row) * a.status0_row_words;
+        for (uint32_t i = threadIdx.x; i < a.status0_row_words; i += kHistBlock) st[i] = 0u;
+    }
     const uint32_t counted = kBytes ? (a.end_bit - a.begin_bit + 7u) / 8u : a.passes;
     for (uint32_t i = threadIdx.x; i < counted * kPassWords; i += kHistBlock) s_h[i] = 0u;
     __syncthreads();
