@@ -297,11 +297,12 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 // ------------------------------------------------------------ launches
 
-// Brackets one launch with events when the call has a timer.
+// One launch, stamped with a timer slot's start and end events when the call
+// has a timer (the dispatch records them; nothing is enqueued between kernels).
 struct TimedLaunch {
-    int idx = -1;
-    const Ctx &c;
-    TimedLaunch(int kind, const Ctx &ctx) : c(ctx) {
+    Launch L;  // the stream, and the slot's events when the call has a timer
+    TimedLaunch(int kind, const Ctx &c) {
+        L.s = c.s;
         lrs_timer *t = c.timer;
         if (t == nullptr || t->used >= kMaxTimed) return;
         const size_t i = t->used;
@@ -312,14 +313,11 @@ struct TimedLaunch {
             t->pool.push_back(a);
             t->pool.push_back(b);
         }
-        if (hipEventRecord(t->pool[2 * i], c.s) != hipSuccess) return;
         t->kind.resize(i + 1);
         t->kind[i] = kind;
         t->used = i + 1;
-        idx = static_cast<int>(i);
-    }
-    void done() {
-        if (idx >= 0) (void)hipEventRecord(c.timer->pool[2 * idx + 1], c.s);
+        L.start = t->pool[2 * i];
+        L.stop = t->pool[2 * i + 1];
     }
 };
 
@@ -327,8 +325,7 @@ struct TimedLaunch {
 template <int KK, int PK>
 hipError_t resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, const Ctx &c) {
     TimedLaunch t(4, c);
-    const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, c.s);
-    t.done();
+    const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, t.L);
     return e;
 }
 
@@ -343,9 +340,8 @@ hipError_t launch_clear(const Plan &p, uint8_t *ws, bool need_hist, const Ctx &c
     const uint64_t words = std::max<uint64_t>(a.words[0] * need_hist, a.words[2]);
     const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(2048, std::max<uint64_t>(1, cdiv(words / 4, kBlock))));
     TimedLaunch t(0, c);
-    clear_kernel<<<blocks, kBlock, 0, c.s>>>(a);
+    launch_on(clear_kernel, dim3(blocks), dim3(kBlock), t.L, a);
     hipError_t e = hipGetLastError();
-    t.done();
     return e;
 }
 
@@ -372,12 +368,11 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     }
     const uint32_t blocks = static_cast<uint32_t>(p.rows * p.hist_chunks_per_row);
     TimedLaunch t(1, c);
-    hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, blocks, c.s)
-                   : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, blocks, c.s)
-                   : (kk == kKeyU64) ? launch_hist<kKeyU64>(p.b, h, blocks, c.s)
-                   : (kk == kKeyX64) ? launch_hist<kKeyX64>(p.b, h, blocks, c.s)
-                                     : launch_hist<kKeyF16>(p.b, h, blocks, c.s);
-    t.done();
+    hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, blocks, t.L)
+                   : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, blocks, t.L)
+                   : (kk == kKeyU64) ? launch_hist<kKeyU64>(p.b, h, blocks, t.L)
+                   : (kk == kKeyX64) ? launch_hist<kKeyX64>(p.b, h, blocks, t.L)
+                                     : launch_hist<kKeyF16>(p.b, h, blocks, t.L);
     return e;
 }
 
@@ -473,9 +468,8 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
         pa.flip_neg = flip_neg;
         {
             TimedLaunch t(1, c);
-            const hipError_t e = (kk == kKeyU32) ? launch_partition_counts<kKeyU32>(p.b, pa, c.s)
-                                                 : launch_partition_counts<kKeyX32>(p.b, pa, c.s);
-            t.done();
+            const hipError_t e = (kk == kKeyU32) ? launch_partition_counts<kKeyU32>(p.b, pa, t.L)
+                                                 : launch_partition_counts<kKeyX32>(p.b, pa, t.L);
             if (e != hipSuccess) return LRS_ERR_HIP;
         }
         uint32_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
@@ -491,14 +485,13 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s)
-                                : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
+                                : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s)
-                                : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, c.s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
+                                : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L);
         }
-        t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;
     }
@@ -571,14 +564,13 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
-                                : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                                : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
-                                : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                                : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
         }
-        t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;
     }
@@ -630,14 +622,13 @@ int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
-                                : launch_sweep<kKeyX64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                                : launch_sweep<kKeyX64, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
             src_v = dv;
         } else {
-            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s)
-                                : launch_sweep<kKeyX64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = (kk == kKeyU64) ? launch_sweep<kKeyU64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                                : launch_sweep<kKeyX64, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
         }
-        t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;
     }
@@ -693,9 +684,8 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
         r.row_len = static_cast<uint32_t>(n);
         r.flip = flip;
         TimedLaunch t(4, c);
-        const hipError_t e = index ? launch_row_resident<kResIndex>(digit_bits, r, c.s)
-                                   : launch_row_resident<kResU32>(digit_bits, r, c.s);
-        t.done();
+        const hipError_t e = index ? launch_row_resident<kResIndex>(digit_bits, r, t.L)
+                                   : launch_row_resident<kResU32>(digit_bits, r, t.L);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -721,7 +711,7 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
             if (pass == 0) {
                 a.keys_in = vals_in;
                 a.keys_out = dw;
-                e = launch_sweep<kKeyF16, kPayPackFirst, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, c.s);
+                e = launch_sweep<kKeyF16, kPayPackFirst, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, t.L);
             } else {
                 // the words' digit fields sit 16 bits above the key's
                 a.shift += 16;
@@ -729,10 +719,9 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
                 const bool last = pass + 1 == p.passes;
                 a.keys_out = last ? static_cast<void *>(vals_out) : static_cast<void *>(dw);
                 a.vals_out = last ? pay_out : nullptr;
-                e = last ? launch_sweep<kKeyU32, kPayUnpackLast, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, c.s)
-                         : launch_sweep<kKeyU32, kPayNone, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, c.s);
+                e = last ? launch_sweep<kKeyU32, kPayUnpackLast, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, t.L)
+                         : launch_sweep<kKeyU32, kPayNone, false>(digit_bits, a, p.tile_cfg, false, p.num_tiles, t.L);
             }
-            t.done();
             if (e != hipSuccess) return LRS_ERR_HIP;
             src_w = dw;
         }
@@ -753,22 +742,21 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
             uint32_t *dp = pass_dst(pass, p.passes, static_cast<uint32_t *>(pay_out), idx[0]);
             a.vals_in = src_p;
             a.vals_out = dp;
-            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
             src_p = dp;
         } else if (pass == 0) {
             a.vals_in = nullptr;
             a.vals_out = idx[0];
-            e = launch_sweep<kKeyF16, kPayIdxFirst, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = launch_sweep<kKeyF16, kPayIdxFirst, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
         } else if (pass + 1 < p.passes) {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = idx[pass & 1];
-            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = launch_sweep<kKeyF16, kPayU32, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
         } else {
             a.vals_in = idx[(pass - 1) & 1];
             a.vals_out = pay_out;
-            e = launch_sweep<kKeyF16, kPayIdxLast, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, c.s);
+            e = launch_sweep<kKeyF16, kPayIdxLast, false>(digit_bits, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
         }
-        t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;
     }
@@ -886,9 +874,8 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
     a.words[0] = p.hist_words;
     {
         TimedLaunch t(0, c);
-        clear_kernel<<<1, kBlock, 0, c.s>>>(a);
+        launch_on(clear_kernel, dim3(1), dim3(kBlock), t.L, a);
         hipError_t e = hipGetLastError();
-        t.done();
         if (e != hipSuccess) return LRS_ERR_HIP;
     }
     if (n == 0) return LRS_OK;
@@ -906,11 +893,9 @@ int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream
     const uint32_t tail = static_cast<uint32_t>(bytes % 16);
     const uint32_t blocks = static_cast<uint32_t>(std::min<uint64_t>(1u << 20, std::max<uint64_t>(1, cdiv(n16, kBlock))));
     TimedLaunch t(3, c);
-    copy_kernel<<<blocks, kBlock, 0, c.s>>>(static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16,
-                                            static_cast<const uint8_t *>(src) + n16 * 16,
-                                            static_cast<uint8_t *>(dst) + n16 * 16, tail);
+    launch_on(copy_kernel, dim3(blocks), dim3(kBlock), t.L, static_cast<const uint4 *>(src), static_cast<uint4 *>(dst),
+              n16, static_cast<const uint8_t *>(src) + n16 * 16, static_cast<uint8_t *>(dst) + n16 * 16, tail);
     hipError_t e = hipGetLastError();
-    t.done();
     return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 

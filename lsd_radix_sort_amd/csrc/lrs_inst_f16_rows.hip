@@ -4,11 +4,11 @@
 
 namespace lrs {
 
-template hipError_t launch_sweep<kKeyF16, kPayIdxFirst, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_sweep<kKeyF16, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_sweep<kKeyF16, kPayIdxLast, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_sweep<kKeyF16, kPayPackFirst, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_hist<kKeyF16>(int, const HistArgs &, uint32_t, hipStream_t);
-template hipError_t launch_row_resident<kResIndex>(int, const RowResidentArgs &, hipStream_t);
-template hipError_t launch_row_resident<kResU32>(int, const RowResidentArgs &, hipStream_t);
+template hipError_t launch_sweep<kKeyF16, kPayIdxFirst, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_sweep<kKeyF16, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_sweep<kKeyF16, kPayIdxLast, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_sweep<kKeyF16, kPayPackFirst, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_hist<kKeyF16>(int, const HistArgs &, uint32_t, const Launch &);
+template hipError_t launch_row_resident<kResIndex>(int, const RowResidentArgs &, const Launch &);
+template hipError_t launch_row_resident<kResU32>(int, const RowResidentArgs &, const Launch &);
 }  // namespace lrs

@@ -5,6 +5,6 @@
 
 namespace lrs {
 
-template hipError_t launch_sweep<kKeyU32, kPayUnpackLast, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
+template hipError_t launch_sweep<kKeyU32, kPayUnpackLast, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
 
 }  // namespace lrs

@@ -4,7 +4,7 @@
 
 namespace lrs {
 
-template hipError_t launch_sweep<kKeyU32, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_sweep<kKeyU32, kPayU32, true>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_resident<kKeyU32, kResU32>(int, const ResidentArgs &, uint64_t, uint64_t, hipStream_t);
+template hipError_t launch_sweep<kKeyU32, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_sweep<kKeyU32, kPayU32, true>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_resident<kKeyU32, kResU32>(int, const ResidentArgs &, uint64_t, uint64_t, const Launch &);
 }  // namespace lrs

@@ -4,7 +4,7 @@
 
 namespace lrs {
 
-template hipError_t launch_sweep<kKeyU64, kPayNone, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_sweep<kKeyU64, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, hipStream_t);
-template hipError_t launch_hist<kKeyU64>(int, const HistArgs &, uint32_t, hipStream_t);
+template hipError_t launch_sweep<kKeyU64, kPayNone, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_sweep<kKeyU64, kPayU32, false>(int, const SweepArgs &, int, bool, uint64_t, const Launch &);
+template hipError_t launch_hist<kKeyU64>(int, const HistArgs &, uint32_t, const Launch &);
 }  // namespace lrs

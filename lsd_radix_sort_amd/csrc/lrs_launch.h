@@ -6,12 +6,27 @@
 // (the driver and C ABI) sees only these declarations.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "lrs_kernels.h"
 
 namespace lrs {
+
+// Where a kernel goes: its stream and, when a caller times it, the events
+// that the dispatch itself stamps with the kernel's start and end (no marker
+// of their own between kernels; null for an untimed launch).
+struct Launch {
+    hipStream_t s = nullptr;
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <typename Kernel, typename... Args>
+inline void launch_on(Kernel kernel, dim3 grid, dim3 block, const Launch &L, Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.start, L.stop, 0, args...);
+}
 
 // Sweep tile shapes (threads x keys per thread).  Long rows use the largest;
 // shorter inputs a smaller one so the grid still has several tiles per CU and
@@ -40,23 +55,23 @@ constexpr TileCfg tile_cfg_of(bool key64, int c, bool keys_only) {
 // PART), tile shape `cfg`, 64-bit look-back words and store addresses when
 // `wide`.
 template <int KK, int PK, bool PART>
-hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t grid, hipStream_t s);
+hipError_t launch_sweep(int b, const SweepArgs &a, int cfg, bool wide, uint64_t grid, const Launch &L);
 
 // All passes' digit counts in one read of the keys.
 template <int KK>
-hipError_t launch_hist(int b, const HistArgs &a, uint32_t blocks, hipStream_t s);
+hipError_t launch_hist(int b, const HistArgs &a, uint32_t blocks, const Launch &L);
 
 // Reduce-then-scan: per-partition counts of one pass digit, then their scan.
 template <int KK>
-hipError_t launch_partition_counts(int b, const PartArgs &pa, hipStream_t s);
+hipError_t launch_partition_counts(int b, const PartArgs &pa, const Launch &L);
 
 // Whole-row resident sort, one workgroup per row (32- and 64-bit keys).
 template <int KK, int PK>
-hipError_t launch_resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, hipStream_t s);
+hipError_t launch_resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, const Launch &L);
 
 // Whole-row sort of 16-bit float rows: as many workgroups as fit on the GPU at
 // once (at most one per row), each looping over rows.
 template <int PK>
-hipError_t launch_row_resident(int b, const RowResidentArgs &a, hipStream_t s);
+hipError_t launch_row_resident(int b, const RowResidentArgs &a, const Launch &L);
 
 }  // namespace lrs
