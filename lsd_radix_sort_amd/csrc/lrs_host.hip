@@ -107,6 +107,9 @@ namespace {
 constexpr uint64_t kMinTiles = LRS_MIN_TILES;
 // Rows up to this length are sorted whole inside one workgroup's LDS.
 constexpr uint64_t kResidentMax = 8192;
+// Whole-row sorts of at most this many elements in all are paced by the host:
+// their timed launch is bracketed by recorded events (see TimedLaunch).
+constexpr uint64_t kHostPacedMax = 65536;
 // Longer index row sorts of rows up to this length carry each element as one
 // 32-bit word, key << 16 | column, between passes.
 constexpr uint64_t kPackedRowMax = 65536;
@@ -297,11 +300,15 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 // ------------------------------------------------------------ launches
 
-// One launch, stamped with a timer slot's start and end events when the call
-// has a timer (the dispatch records them; nothing is enqueued between kernels).
+// One launch, timed into a timer slot when the call has a timer.  Normally
+// the dispatch itself stamps the slot's events, so nothing is enqueued
+// between dependent kernels; a small sort done in one launch, which the host
+// rather than the GPU paces, brackets the launch with recorded events instead
+// (less host time per launch).
 struct TimedLaunch {
-    Launch L;  // the stream, and the slot's events when the call has a timer
-    TimedLaunch(int kind, const Ctx &c) {
+    Launch L;  // the stream, and the slot's events when the dispatch stamps them
+    hipEvent_t after = nullptr;  // bracketing: recorded by done()
+    TimedLaunch(int kind, const Ctx &c, bool bracket = false) {
         L.s = c.s;
         lrs_timer *t = c.timer;
         if (t == nullptr || t->used >= kMaxTimed) return;
@@ -313,19 +320,28 @@ struct TimedLaunch {
             t->pool.push_back(a);
             t->pool.push_back(b);
         }
+        if (bracket) {
+            if (hipEventRecord(t->pool[2 * i], c.s) != hipSuccess) return;
+            after = t->pool[2 * i + 1];
+        } else {
+            L.start = t->pool[2 * i];
+            L.stop = t->pool[2 * i + 1];
+        }
         t->kind.resize(i + 1);
         t->kind[i] = kind;
         t->used = i + 1;
-        L.start = t->pool[2 * i];
-        L.stop = t->pool[2 * i + 1];
+    }
+    void done() {
+        if (after != nullptr) (void)hipEventRecord(after, L.s);
     }
 };
 
 // Whole-row resident sort, timed as kind 4.
 template <int KK, int PK>
 hipError_t resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, const Ctx &c) {
-    TimedLaunch t(4, c);
+    TimedLaunch t(4, c, rows * row_len <= kHostPacedMax);
     const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, t.L);
+    t.done();
     return e;
 }
 
@@ -683,9 +699,10 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
         r.rows = static_cast<uint32_t>(rows);
         r.row_len = static_cast<uint32_t>(n);
         r.flip = flip;
-        TimedLaunch t(4, c);
+        TimedLaunch t(4, c, static_cast<uint64_t>(rows) * n <= kHostPacedMax);
         const hipError_t e = index ? launch_row_resident<kResIndex>(digit_bits, r, t.L)
                                    : launch_row_resident<kResU32>(digit_bits, r, t.L);
+        t.done();
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
     }
     uint8_t *ws = static_cast<uint8_t *>(workspace);
