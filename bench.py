@@ -17,12 +17,14 @@ f64_pairs_2p27_asc, u32_pairs_2p29_uniform, u32_pairs_2p30_uniform.
 
 roofline: the dominant kernel is the sweep (one LSD pass).  achieved = the
 algorithmic bytes of the sweep launches of one sort (pairs: 16 B per pair per
-pass; keys: 8 B per key per pass; fp16/bf16 rows: 8, 12, ..., 16 B per element
-from the first to the last pass) / their summed duration, from HIP events the
-library records around each sweep launch inside the timed region.  Rows of at
-most 8192 elements are sorted by one whole-row resident launch instead (read
-once, write once: 8 B/key, 16 B/pair, 12 B per fp16/bf16 element with its
-int64 index).
+pass; keys: 8 B per key per pass; 8-byte keys with a u32 value: 24 B; fp16/bf16
+rows of at most 65,536 with their int64 index, which travel between passes as
+one word key << 16 | column: 6, 8, ..., 8, 14 B per element from the first to
+the last pass; longer rows 8, 12, ..., 12, 16 B) / their summed duration, from
+HIP events on the sort's stream inside the timed region (stamped by the timed
+dispatches themselves).  Rows of at most 8192 elements are sorted by one
+whole-row resident launch instead (read once, write once: 8 B/key, 16 B/pair,
+12 B per fp16/bf16 element with its int64 index).
 """
 from __future__ import annotations
 

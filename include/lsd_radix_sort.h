@@ -266,8 +266,11 @@ int radix_sort_pairs_no_alloc(const uint32_t *keys_in, const uint32_t *vals_in, 
 /*
  * Kernel timing for measurement (opts->timer).  radix_sort_timer_create
  * returns a new timer (NULL if host memory runs out); calls given it in their
- * options bracket each kernel they enqueue with HIP events on their stream.
- * radix_sort_timer_read waits for the recorded events and reports, per kernel
+ * options time each kernel they enqueue with a pair of HIP events on their
+ * stream, stamped by the kernel's dispatch itself (a whole sort of at most
+ * 65,536 elements done in one launch records the pair just before and after
+ * that launch instead; a reduce-then-scan pass's count and scan kernels share
+ * one pair).  radix_sort_timer_read waits for the events and reports, per kernel
  * kind (0 = workspace clear, 1 = digit histogram and the reduce-then-scan
  * count and scan, 2 = sweep/scatter pass, 3 = copy probe, 4 = whole-row
  * resident sort), the summed milliseconds and the number of launches in the

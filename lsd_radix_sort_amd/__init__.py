@@ -132,7 +132,9 @@ def _bad(msg: str):
 
 class KernelTimer:
     """A library kernel timer (lrs_timer): pass it in SortOptions(timer=...) and
-    every kernel those calls enqueue is bracketed by HIP events on its stream.
+    every kernel those calls enqueue is timed by a pair of HIP events on its
+    stream (stamped by the dispatch; recorded around the launch for whole sorts
+    of at most 65,536 elements done in one launch).
 
     As a context manager, ``ms`` and ``launches`` hold per-kind sums ("clear",
     "histogram", "sweep", "copy", "resident") after exit; ``read()`` returns
