@@ -270,7 +270,9 @@ int radix_sort_pairs_no_alloc(const uint32_t *keys_in, const uint32_t *vals_in, 
  * stream, stamped by the kernel's dispatch itself (a whole sort of at most
  * 65,536 elements done in one launch records the pair just before and after
  * that launch instead; a reduce-then-scan pass's count and scan kernels share
- * one pair).  radix_sort_timer_read waits for the events and reports, per kernel
+ * one pair).  The events carry no system-scope fence: they time the work but
+ * do not make its results visible to the host (synchronize the stream for
+ * that).  radix_sort_timer_read waits for the events and reports, per kernel
  * kind (0 = workspace clear, 1 = digit histogram and the reduce-then-scan
  * count and scan, 2 = sweep/scatter pass, 3 = copy probe, 4 = whole-row
  * resident sort), the summed milliseconds and the number of launches in the

@@ -214,12 +214,21 @@ def _opt(options: SortOptions | None):
 
 # --------------------------------------------------------------- validation
 
-def _stream(t: torch.Tensor) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+# torch's own getter of the current stream's raw handle (the public
+# torch.cuda.current_stream(...).cuda_stream builds a Stream object and costs
+# about 2 us a call, as much as a small sort's whole launch)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _stream(t: torch.Tensor) -> int:
+    """The handle of torch's current stream on t's device."""
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
 
 
 def _gpu_input(t, name: str):

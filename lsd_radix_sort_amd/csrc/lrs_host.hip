@@ -314,9 +314,14 @@ struct TimedLaunch {
         if (t == nullptr || t->used >= kMaxTimed) return;
         const size_t i = t->used;
         if (t->pool.size() < 2 * (i + 1)) {
+            // The events only time: without the system-scope fence a recorded
+            // event would otherwise add (a cache write-back and invalidation).
             hipEvent_t a, b;
-            if (hipEventCreate(&a) != hipSuccess) return;
-            if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+            if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
+            if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
+                (void)hipEventDestroy(a);
+                return;
+            }
             t->pool.push_back(a);
             t->pool.push_back(b);
         }
