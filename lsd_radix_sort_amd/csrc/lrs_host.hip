@@ -109,7 +109,10 @@ constexpr uint64_t kMinTiles = LRS_MIN_TILES;
 constexpr uint64_t kResidentMax = 8192;
 // Whole-row sorts of at most this many elements in all are paced by the host:
 // their timed launch is bracketed by recorded events (see TimedLaunch).
-constexpr uint64_t kHostPacedMax = 65536;
+#ifndef LRS_HOST_PACED_MAX
+#define LRS_HOST_PACED_MAX 65536
+#endif
+constexpr uint64_t kHostPacedMax = LRS_HOST_PACED_MAX;
 // Longer index row sorts of rows up to this length carry each element as one
 // 32-bit word, key << 16 | column, between passes.
 constexpr uint64_t kPackedRowMax = 65536;
