@@ -105,10 +105,12 @@ typedef enum lrs_status {
  *                   that are sorted by sweeps (more than 8192 elements) take
  *                   it as well (a test hook; the result is identical).  Pass
  *                   the same options to the workspace-size query.
- * timer             If not NULL, every kernel the call enqueues is bracketed by
+ * timer             If not NULL, every kernel the call enqueues is timed by
  *                   HIP events on its stream and recorded in this timer (see
  *                   radix_sort_timer_create).  A timer must not be used by two
- *                   calls at the same time.
+ *                   calls at the same time.  Timing is for calls run eagerly:
+ *                   a timed call on a stream that is being captured into a
+ *                   graph returns LRS_ERR_OPTION and enqueues nothing.
  */
 #define LRS_SCAN_LOOKBACK 0
 #define LRS_SCAN_REDUCE_THEN_SCAN 1

@@ -178,6 +178,12 @@ bool make_ctx(void *stream, const lrs_options *o, Ctx &c) {
     if (o->scan_strategy != LRS_SCAN_LOOKBACK && o->scan_strategy != LRS_SCAN_REDUCE_THEN_SCAN) return false;
     c.scan = o->scan_strategy;
     c.timer = o->timer;
+    // Timer events are for calls run eagerly: a timed call on a stream being
+    // captured into a graph is refused before anything is enqueued.
+    if (c.timer != nullptr && c.s != nullptr) {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(c.s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return false;
+    }
     if (o->spin_limit != 0) c.spin_limit = o->spin_limit;
     if (o->prefix_from_keys) c.spin_limit = 0;
     c.wide_from = o->wide_from;

@@ -2,7 +2,8 @@
 
 The kernel timer (radix_sort_timer_*) must count every kernel a timed call
 enqueues under its kind, give each a positive time, empty itself on read and
-leave the sort's result exact (against the oracle).  The copy probe
+leave the sort's result exact (against the oracle), and be refused (with
+nothing enqueued) on a stream that is being captured into a graph.  The copy probe
 (radix_sort_copy_probe) must copy exactly the bytes asked for, tails of fewer
 than 16 bytes included, write nothing past them, and reject misaligned or
 overlapping buffers before launching anything."""
@@ -185,3 +186,45 @@ def test_copy_probe_rejects_bad_buffers():
         lrs.copy_probe(buf[:2048], dst[:1024])     # destination too small
     torch.cuda.synchronize()
     assert int(dst.sum()) == 0, "a rejected copy wrote"
+
+
+def test_timed_call_refused_during_graph_capture():
+    # a timer's events are for eager calls: under capture the timed call is
+    # refused before it enqueues anything, while the same call untimed is
+    # captured and its replays sort correctly
+    n = 100000
+    keys = workloads.random_u32(7600, n)
+    kin = to_gpu_u32(keys)
+    kout = torch.empty_like(kin)
+    ws = torch.empty(lrs.radix_sort_workspace_size(n, 0, 32, 8), dtype=torch.uint8, device=kin.device)
+    timer = lrs.KernelTimer()
+    try:
+        lrs.radix_sort_keys(kin, 0, 32, 8, out=kout, workspace=ws)  # eager call before capture
+        torch.cuda.synchronize()
+        kout.zero_()
+        refused = None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            try:
+                lrs.radix_sort_keys(kin, 0, 32, 8, out=kout, workspace=ws, options=lrs.SortOptions(timer=timer))
+            except lrs.RadixSortArgumentError as e:
+                refused = e
+            lrs.radix_sort_keys(kin, 0, 32, 8, out=kout, workspace=ws)
+        torch.cuda.synchronize()
+        assert refused is not None and refused.status == 10, f"timed call under capture: {refused!r}"
+        ms, launches = timer.read()
+        assert all(v == 0 for v in launches.values()), "the refused call recorded launches"
+        expect = oracle.radix_sort_keys(keys, 0, 32, 8)
+        for rep in range(3):
+            kout.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np_u32(kout), expect), f"replay {rep}"
+        # and the timer still works eagerly afterwards
+        with timer:
+            lrs.radix_sort_keys(kin, 0, 32, 8, out=kout, workspace=ws, options=lrs.SortOptions(timer=timer))
+        assert timer.launches["sweep"] == 4
+        assert np.array_equal(to_np_u32(kout), expect)
+    finally:
+        timer.close()
