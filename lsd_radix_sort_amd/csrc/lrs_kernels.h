@@ -210,6 +210,18 @@ template <> struct BufIO<int64_t> {
 // from sinking its computation and keeping the operands alive instead).
 __device__ inline void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
 
+// Store v as element i of a row too long for a buffer resource (row is the
+// same for the whole workgroup).  With kOff32 (every byte offset of the row
+// fits in 32 bits) the address is the row's scalar base plus a 32-bit byte
+// offset, which the store adds itself; otherwise a 64-bit address.
+template <bool kOff32, typename T>
+__device__ inline void wide_store(T *row, uint32_t i, T v) {
+    if constexpr (kOff32)
+        *reinterpret_cast<T *>(reinterpret_cast<char *>(row) + i * static_cast<uint32_t>(sizeof(T))) = v;
+    else
+        row[i] = v;
+}
+
 // --------------------------------------------------------- wave utilities
 
 // Lanes of this wave whose digit equals this lane's digit (all 64 lanes must
@@ -779,7 +791,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                       PK == kPayUnpackLast ? a.row_len * 8u : 0u);
         // Without the bounds select (full tiles) the loop has no branches and
         // all of a thread's slot reads can be in flight at once.
-        auto keys_out = [&](auto partial) {
+        auto keys_out = [&](auto partial, auto off32) {
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
                 const uint32_t k = i * BLOCK + tid;
@@ -796,14 +808,29 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                                                                        static_cast<uint32_t>(a.flip)));
                     BufIO<int64_t>::store(iout_rsrc, dst, static_cast<uint32_t>(v) & 0xFFFFu);
                 } else if constexpr (kWide) {
-                    if (dst < a.row_len) kout[dst] = static_cast<Stored>(v);
+                    // (every slot of a full tile holds a real element)
+                    if (!decltype(partial)::value || dst < a.row_len)
+                        wide_store<decltype(off32)::value>(kout, dst, static_cast<Stored>(v));
                 } else {
                     BufIO<Stored>::store(kout_rsrc, dst, v);
                 }
             }
         };
-        if (valid == TILE) keys_out(std::false_type{});
-        else keys_out(std::true_type{});
+        // Wide rows whose byte offsets all fit in 32 bits store through 32-bit
+        // offsets (one copy of each loop per address form, no per-slot test).
+        const bool keys_off32 = static_cast<uint64_t>(a.row_len) * sizeof(Stored) <= (uint64_t(1) << 32);
+        if constexpr (kWide) {
+            if (keys_off32) {
+                if (valid == TILE) keys_out(std::false_type{}, std::true_type{});
+                else keys_out(std::true_type{}, std::true_type{});
+            } else {
+                if (valid == TILE) keys_out(std::false_type{}, std::false_type{});
+                else keys_out(std::true_type{}, std::false_type{});
+            }
+        } else {
+            if (valid == TILE) keys_out(std::false_type{}, std::false_type{});
+            else keys_out(std::true_type{}, std::false_type{});
+        }
 
         // The payload is loaded only now, after the keys have gone out (loading
         // it before the look-back, to overlap that wait, measured 0.3% slower on
@@ -829,14 +856,30 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             using OutT = typename std::conditional<PK == kPayIdxLast, int64_t, uint32_t>::type;
             OutT *vout = static_cast<OutT *>(a.vals_out) + row_base;
             const __amdgpu_buffer_rsrc_t vout_rsrc = make_rsrc(vout, kWide ? 0u : a.row_len * sizeof(OutT));
+            if constexpr (kWide) {
+                // full tiles without the bounds test (no branch per slot)
+                auto pay_out = [&](auto partial, auto off32) {
 #pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                const uint32_t k = i * BLOCK + tid;
-                const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
-                const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
-                if constexpr (kWide) {
-                    if (dst < a.row_len) vout[dst] = static_cast<OutT>(s_pay[k]);
+                    for (int i = 0; i < ITEMS; ++i) {
+                        const uint32_t k = i * BLOCK + tid;
+                        const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
+                        if (!decltype(partial)::value || k < valid)
+                            wide_store<decltype(off32)::value>(vout, s_goff[d] + k, static_cast<OutT>(s_pay[k]));
+                    }
+                };
+                if (static_cast<uint64_t>(a.row_len) * sizeof(OutT) <= (uint64_t(1) << 32)) {
+                    if (valid == TILE) pay_out(std::false_type{}, std::true_type{});
+                    else pay_out(std::true_type{}, std::true_type{});
                 } else {
+                    if (valid == TILE) pay_out(std::false_type{}, std::false_type{});
+                    else pay_out(std::true_type{}, std::false_type{});
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < ITEMS; ++i) {
+                    const uint32_t k = i * BLOCK + tid;
+                    const uint32_t d = (slot_digits[i / 4] >> (8 * (i % 4))) & 0xFFu;
+                    const uint32_t dst = (k < valid) ? s_goff[d] + k : 0xFFFFFFFFu;
                     BufIO<OutT>::store(vout_rsrc, dst, s_pay[k]);
                 }
             }
