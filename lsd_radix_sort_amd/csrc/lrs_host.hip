@@ -107,8 +107,8 @@ namespace {
 constexpr uint64_t kMinTiles = LRS_MIN_TILES;
 // Rows up to this length are sorted whole inside one workgroup's LDS.
 constexpr uint64_t kResidentMax = 8192;
-// Whole-row sorts of at most this many elements in all are paced by the host:
-// their timed launch is bracketed by recorded events (see TimedLaunch).
+// Calls over at most this many elements are paced by the host: their timed
+// launches are bracketed by recorded events (see TimedLaunch).
 #ifndef LRS_HOST_PACED_MAX
 #define LRS_HOST_PACED_MAX 65536
 #endif
@@ -169,6 +169,7 @@ struct Ctx {
     uint32_t spin_limit = kDefaultSpinLimit;  // 0: every tile counts its prefix from the keys
     int scan = LRS_SCAN_LOOKBACK;
     uint64_t wide_from = 0;
+    uint64_t elems = ~uint64_t(0);  // elements the call handles (sets how a timer times it)
 };
 
 // False for an invalid option.
@@ -309,18 +310,23 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 // ------------------------------------------------------------ launches
 
-// One launch, timed into a timer slot when the call has a timer.  Normally
-// the dispatch itself stamps the slot's events, so nothing is enqueued
-// between dependent kernels; a small sort done in one launch, which the host
-// rather than the GPU paces, brackets the launch with recorded events instead
-// (less host time per launch).
+// One launch, timed into a timer slot when the call has a timer.  For calls
+// over many elements the dispatch itself stamps the slot's events, so nothing
+// is enqueued between dependent kernels.  Calls over at most kHostPacedMax
+// elements, whose launches the host rather than the GPU paces, bracket each
+// launch with recorded events instead, which cost the host less per launch;
+// the closing event is recorded when the TimedLaunch goes out of scope, so
+// its scope must end right after the launch.
 struct TimedLaunch {
     Launch L;  // the stream, and the slot's events when the dispatch stamps them
-    hipEvent_t after = nullptr;  // bracketing: recorded by done()
-    TimedLaunch(int kind, const Ctx &c, bool bracket = false) {
+    hipEvent_t after = nullptr;  // bracketing: recorded by done() or on scope exit
+    TimedLaunch(const TimedLaunch &) = delete;
+    TimedLaunch &operator=(const TimedLaunch &) = delete;
+    explicit TimedLaunch(int kind, const Ctx &c) {
         L.s = c.s;
         lrs_timer *t = c.timer;
         if (t == nullptr || t->used >= kMaxTimed) return;
+        const bool bracket = c.elems <= kHostPacedMax;
         const size_t i = t->used;
         if (t->pool.size() < 2 * (i + 1)) {
             // The events only time: without the system-scope fence a recorded
@@ -347,13 +353,15 @@ struct TimedLaunch {
     }
     void done() {
         if (after != nullptr) (void)hipEventRecord(after, L.s);
+        after = nullptr;
     }
+    ~TimedLaunch() { done(); }
 };
 
 // Whole-row resident sort, timed as kind 4.
 template <int KK, int PK>
 hipError_t resident(int b, const ResidentArgs &a, uint64_t rows, uint64_t row_len, const Ctx &c) {
-    TimedLaunch t(4, c, rows * row_len <= kHostPacedMax);
+    TimedLaunch t(4, c);
     const hipError_t e = launch_resident<KK, PK>(b, a, rows, row_len, t.L);
     t.done();
     return e;
@@ -535,6 +543,7 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
             int end_bit, int b, void *workspace, size_t ws_bytes, void *stream, const lrs_options *opts) {
     Ctx c;
     if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
+    c.elems = n;
     if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
@@ -615,6 +624,7 @@ int sort_64(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint64_t
             int end_bit, int b, void *workspace, size_t ws_bytes, void *stream, const lrs_options *opts) {
     Ctx c;
     if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
+    c.elems = n;
     if (!digit_bits_ok(b)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 64 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
@@ -682,6 +692,7 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
              void *stream, const lrs_options *opts) {
     Ctx c;
     if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
+    c.elems = static_cast<uint64_t>(rows < 0 ? 0 : rows) * static_cast<uint64_t>(n < 0 ? 0 : n);
     const int st = check_rows(rows, n, dtype, digit_bits);
     if (st != LRS_OK) return st;
     if (rows == 0 || n == 0) return LRS_OK;
@@ -713,7 +724,7 @@ int row_sort(const uint16_t *vals_in, const uint32_t *pay_in, uint16_t *vals_out
         r.rows = static_cast<uint32_t>(rows);
         r.row_len = static_cast<uint32_t>(n);
         r.flip = flip;
-        TimedLaunch t(4, c, static_cast<uint64_t>(rows) * n <= kHostPacedMax);
+        TimedLaunch t(4, c);
         const hipError_t e = index ? launch_row_resident<kResIndex>(digit_bits, r, t.L)
                                    : launch_row_resident<kResU32>(digit_bits, r, t.L);
         t.done();
@@ -894,6 +905,7 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
                                 uint32_t *hist_out, void *stream, const lrs_options *opts) {
     Ctx c;
     if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
+    c.elems = n;
     if (!digit_bits_ok(digit_bits)) return LRS_ERR_DIGIT_BITS;
     if (begin_bit < 0 || end_bit > 32 || begin_bit >= end_bit) return LRS_ERR_BIT_RANGE;
     if (n > LRS_MAX_KEYS) return LRS_ERR_SIZE;
@@ -916,6 +928,7 @@ int radix_sort_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit,
 int radix_sort_copy_probe(const void *src, void *dst, size_t bytes, void *stream, const lrs_options *opts) {
     Ctx c;
     if (!make_ctx(stream, opts, c)) return LRS_ERR_OPTION;
+    c.elems = bytes / 4;
     if (bytes == 0) return LRS_OK;
     if (!src || !dst) return LRS_ERR_NULL_POINTER;
     if (misaligned(src, 16) || misaligned(dst, 16)) return LRS_ERR_ALIGNMENT;

@@ -6,27 +6,13 @@
 // (the driver and C ABI) sees only these declarations.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lrs_dispatch.h"
 #include "lrs_kernels.h"
 
 namespace lrs {
-
-// Where a kernel goes: its stream and, when a caller times it, the events
-// that the dispatch itself stamps with the kernel's start and end (no marker
-// of their own between kernels; null for an untimed launch).
-struct Launch {
-    hipStream_t s = nullptr;
-    hipEvent_t start = nullptr;
-    hipEvent_t stop = nullptr;
-};
-
-template <typename Kernel, typename... Args>
-inline void launch_on(Kernel kernel, dim3 grid, dim3 block, const Launch &L, Args... args) {
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.start, L.stop, 0, args...);
-}
 
 // Sweep tile shapes (threads x keys per thread).  Long rows use the largest;
 // shorter inputs a smaller one so the grid still has several tiles per CU and
