@@ -1207,6 +1207,9 @@ struct HistArgs {
 
 constexpr int kHistMaxCounters = 2048;  // passes * R for every legal (window, b, key width)
 constexpr int kHistCopies = LRS_HIST_COPIES;
+#ifndef LRS_HIST_UNROLL
+#define LRS_HIST_UNROLL 4
+#endif
 #ifndef LRS_HIST_BLOCK
 #define LRS_HIST_BLOCK 1024
 #endif
@@ -1242,7 +1245,7 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
     // half the copies when the counters would not fit in 128 KB (8-bit digits of 64-bit keys)
     constexpr int kCopies = (kMaxCounted * kCR * kHistCopies * 4 <= 131072) ? kHistCopies : kHistCopies / 2;
     constexpr uint32_t kPassWords = kCR * kCopies;
-    constexpr int kUnroll = 4;
+    constexpr int kUnroll = LRS_HIST_UNROLL;  // 16-byte loads each thread has in flight
     __shared__ uint32_t s_h[kMaxCounted * kCR * kCopies];  // 128 KB for u32 keys
     // byte counts summed over the copies, from which the passes' counts fold
     __shared__ uint32_t s_byte[kBytes ? kMaxCounted * kCR : 1];
