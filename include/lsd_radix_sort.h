@@ -269,10 +269,10 @@ int radix_sort_pairs_no_alloc(const uint32_t *keys_in, const uint32_t *vals_in, 
  * Kernel timing for measurement (opts->timer).  radix_sort_timer_create
  * returns a new timer (NULL if host memory runs out); calls given it in their
  * options time each kernel they enqueue with a pair of HIP events on their
- * stream, stamped by the kernel's dispatch itself (a whole sort of at most
- * 65,536 elements done in one launch records the pair just before and after
- * that launch instead; a reduce-then-scan pass's count and scan kernels share
- * one pair).  The events carry no system-scope fence: they time the work but
+ * stream, stamped by the kernel's dispatch itself (a call over at most 65,536
+ * elements, or 65,536 four-byte words for the copy probe, records the pair
+ * just before and after each launch instead; a reduce-then-scan pass's count
+ * and scan kernels share one pair).  The events carry no system-scope fence: they time the work but
  * do not make its results visible to the host (synchronize the stream for
  * that).  radix_sort_timer_read waits for the events and reports, per kernel
  * kind (0 = workspace clear, 1 = digit histogram and the reduce-then-scan

@@ -133,8 +133,8 @@ def _bad(msg: str):
 class KernelTimer:
     """A library kernel timer (lrs_timer): pass it in SortOptions(timer=...) and
     every kernel those calls enqueue is timed by a pair of HIP events on its
-    stream (stamped by the dispatch; recorded around the launch for whole sorts
-    of at most 65,536 elements done in one launch).
+    stream (stamped by the dispatch; recorded around each launch for calls
+    over at most 65,536 elements).
 
     As a context manager, ``ms`` and ``launches`` hold per-kind sums ("clear",
     "histogram", "sweep", "copy", "resident") after exit; ``read()`` returns
