@@ -397,12 +397,33 @@ __device__ inline void load_run(Word (&key)[ITEMS], __amdgpu_buffer_rsrc_t r, ui
 // column of counters cnt[d * BLOCK + t] (R * BLOCK words of LDS); its items of
 // one digit rank in item order.  rank[j] = digit << 16 | rank among the
 // thread's items of that digit.
+#ifndef LRS_COUNT_PAIRS
+#define LRS_COUNT_PAIRS 1
+#endif
 template <uint32_t R, int ITEMS, int BLOCK, typename Dig>
 __device__ inline void thread_count_digits(Dig dig, uint32_t (&rank)[ITEMS], uint32_t *cnt, int tid) {
 #pragma unroll
     for (uint32_t d = 0; d < R; ++d) cnt[d * BLOCK + tid] = 0u;
+    int j = 0;
+    if constexpr (LRS_COUNT_PAIRS) {
+        // Two items per step: both counters are read before either is
+        // written, so each step waits for one LDS round trip instead of two.
+        // Items of equal digits: the second ranks one above the first, and
+        // the second write (issued after the first) leaves the count at +2.
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
+        for (; j + 1 < ITEMS; j += 2) {
+            const uint32_t d0 = dig(j), d1 = dig(j + 1);
+            const uint32_t c0 = cnt[d0 * BLOCK + tid];
+            const uint32_t c1 = cnt[d1 * BLOCK + tid];
+            const bool same = d0 == d1;
+            cnt[d0 * BLOCK + tid] = c0 + 1u;
+            cnt[d1 * BLOCK + tid] = same ? c0 + 2u : c1 + 1u;
+            rank[j] = (d0 << 16) | c0;
+            rank[j + 1] = (d1 << 16) | (same ? c0 + 1u : c1);
+        }
+    }
+#pragma unroll
+    for (; j < ITEMS; ++j) {
         const uint32_t d = dig(j);
         const uint32_t before = cnt[d * BLOCK + tid];
         cnt[d * BLOCK + tid] = before + 1u;
