@@ -245,8 +245,8 @@ def graph_sweep(sizes, digit_bits: int, reps: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--dist", default=None, choices=["uniform", "and3"],
                     help="shorthand for the 2^28-pair workload with this key distribution")
