@@ -47,6 +47,9 @@ namespace lrs {
 #ifndef LRS_SWEEP_WAVES_PER_EU
 #define LRS_SWEEP_WAVES_PER_EU 4  // register budget of the sweep (4: 128 VGPRs)
 #endif
+#ifndef LRS_PAYLOAD_EARLY
+#define LRS_PAYLOAD_EARLY 2     // payload loads before the key write-out: 0 never, 1 always, 2 for 8-byte keys
+#endif
 
 
 constexpr int kBlock = 256;            // threads per workgroup (histogram, utilities)
@@ -837,6 +840,17 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                 }
             }
         };
+        // 8-byte keys: the payload's loads go out before the key write-out and
+        // are in flight during it (3% faster on 2^27 f64 pairs; 2% slower on
+        // 2^28 u32 pairs, whose payload is loaded after the keys have gone out)
+        constexpr bool kPayEarly = LRS_PAYLOAD_EARLY == 1 || (LRS_PAYLOAD_EARLY == 2 && sizeof(Stored) == 8);
+        uint32_t val[ITEMS];
+        if constexpr (kPayEarly && (PK == kPayU32 || PK == kPayIdxLast)) {
+            const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
+            const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) val[j] = BufIO<uint32_t>::load(vin_rsrc, wbase + j * kWave + lane);
+        }
         // Wide rows whose byte offsets all fit in 32 bits store through 32-bit
         // offsets (one copy of each loop per address form, no per-slot test).
         const bool keys_off32 = static_cast<uint64_t>(a.row_len) * sizeof(Stored) <= (uint64_t(1) << 32);
@@ -853,11 +867,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             else keys_out(std::true_type{}, std::false_type{});
         }
 
-        // The payload is loaded only now, after the keys have gone out (loading
-        // it before the look-back, to overlap that wait, measured 0.3% slower on
-        // uniform 2^28 pairs and 4% slower with AND-of-3 keys).
-        uint32_t val[ITEMS];
-        if constexpr (PK == kPayU32 || PK == kPayIdxLast) {
+        // Otherwise the payload is loaded only now, after the keys have gone out
+        // (loading it before the look-back, to overlap that wait, measured 0.3%
+        // slower on uniform 2^28 pairs and 4% slower with AND-of-3 keys).
+        if constexpr (!kPayEarly && (PK == kPayU32 || PK == kPayIdxLast)) {
             const uint32_t *vin = static_cast<const uint32_t *>(a.vals_in) + row_base + tile_start;
             const __amdgpu_buffer_rsrc_t vin_rsrc = make_rsrc(vin, valid * 4u);
 #pragma unroll
