@@ -1417,28 +1417,42 @@ __global__ __launch_bounds__(kHistBlock) void histogram_kernel(HistArgs a) {
         __syncthreads();
         if (s_last == 0u) return;
     }
-    // Thread i scans counts 2i and 2i+1 (R is even, so every pass starts at an
-    // even index); one scan runs over all passes at once and each pass then
-    // subtracts the prefix at its first digit (exact modulo 2^32).
-    static_assert(2 * kHistBlock >= kHistMaxCounters, "two counts per thread cover every pass");
-    uint32_t c0 = 0u, c1 = 0u;
-    const uint32_t i0 = 2u * threadIdx.x;
+    // Thread t scans counts K t .. K t + K - 1; one scan runs over all passes
+    // at once and each pass then subtracts the prefix at its first digit
+    // (exact modulo 2^32).
+    constexpr uint32_t K = kHistMaxCounters / kHistBlock;
+    static_assert(K * kHistBlock == kHistMaxCounters, "K counts per thread cover every pass");
     auto final_count = [&](uint32_t i) -> uint32_t {
         if (i >= total) return 0u;
         return a.atomic ? __hip_atomic_load(out + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lds_count(i);
     };
-    c0 = final_count(i0);
-    c1 = final_count(i0 + 1u);
+    const uint32_t i0 = K * threadIdx.x;
+    uint32_t c[K];
+    uint32_t sum = 0u;
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) {
+        c[k] = final_count(i0 + k);
+        sum += c[k];
+    }
     __shared__ uint32_t s_scan[kHistBlock / kWave];
     __shared__ uint32_t s_pass_start[kHistMaxCounters / 2];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const uint32_t e0 = block_exclusive_scan_n<kHistBlock, false>(c0 + c1, s_scan, lane, wave);
-    if (i0 < total && i0 % R == 0) s_pass_start[i0 / R] = e0;
+    const uint32_t e0 = block_exclusive_scan_n<kHistBlock, false>(sum, s_scan, lane, wave);
+    uint32_t run = e0;
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) {
+        if (i0 + k < total && (i0 + k) % R == 0) s_pass_start[(i0 + k) / R] = run;
+        run += c[k];
+    }
     __syncthreads();
     uint32_t *bases = a.bases + static_cast<uint64_t>(row) * total;
-    if (i0 < total) bases[i0] = e0 - s_pass_start[i0 / R];
-    if (i0 + 1u < total) bases[i0 + 1u] = e0 + c0 - s_pass_start[i0 / R];
+    run = e0;
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) {
+        if (i0 + k < total) bases[i0 + k] = run - s_pass_start[(i0 + k) / R];
+        run += c[k];
+    }
 }
 
 // --------------------------------------------- reduce-then-scan, per pass
