@@ -50,6 +50,9 @@ namespace lrs {
 #ifndef LRS_PAYLOAD_EARLY
 #define LRS_PAYLOAD_EARLY 2     // payload loads before the key write-out: 0 never, 1 always, 2 for 8-byte keys
 #endif
+#ifndef LRS_RANK_PIPELINE
+#define LRS_RANK_PIPELINE 1     // ballot rank builds item j+1's match mask while item j's counter read is in flight
+#endif
 
 
 constexpr int kBlock = 256;            // threads per workgroup (histogram, utilities)
@@ -268,6 +271,52 @@ __device__ inline uint32_t count_below(uint64_t m) {
 __device__ inline void group_rank(uint64_t members, uint32_t &below, uint32_t &size) {
     below = count_below(members);
     size = static_cast<uint32_t>(__popcll(members));
+}
+
+// Stable rank of a wave's ITEMS digits per lane, items in order of j, then of
+// lane: out(j, d, r) receives item j's digit d and r = the count of the
+// wave's earlier items with digit d, read from the wave's own counters cnt[],
+// which advance by each digit group's size (its lowest lane writes).  The
+// counter read of item j depends on the write of item j - 1; building the
+// match mask of item j + 1 between that read and its use keeps the LDS round
+// trip from stalling the wave (the pins inside match_mask hold the read before
+// them, and an empty asm that takes the read and the new mask holds its use
+// after).  kPipe = false ranks item by item (fewer live registers).
+template <int B, int ITEMS, bool kPipe, typename DigitFn, typename OutFn>
+__device__ inline void wave_rank(DigitFn digit, uint32_t *cnt, OutFn out) {
+    if constexpr (LRS_RANK_PIPELINE && kPipe) {
+        uint32_t d = digit(0);
+        uint64_t m = match_mask<B>(d);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            uint32_t before = cnt[d];
+            uint32_t d_next = 0u;
+            uint64_t m_next = 0u;
+            if (j + 1 < ITEMS) {
+                d_next = digit(j + 1);
+                m_next = match_mask<B>(d_next);
+                // the read is used only once the next mask is built
+                asm volatile("" : "+v"(before) : "v"(static_cast<uint32_t>(m_next)),
+                             "v"(static_cast<uint32_t>(m_next >> 32)));
+            }
+            uint32_t below, size;
+            group_rank(m, below, size);
+            out(j, d, before + below);
+            if (below == 0u) cnt[d] = before + size;
+            d = d_next;
+            m = m_next;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t d = digit(j);
+            uint32_t below, size;
+            group_rank(match_mask<B>(d), below, size);
+            const uint32_t before = cnt[d];
+            out(j, d, before + below);
+            if (below == 0u) cnt[d] = before + size;
+        }
+    }
 }
 
 // Inclusive sum over the lanes of a wave (all 64 lanes active), by DPP lane
@@ -653,18 +702,18 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             // wave's running count of the digit.
             // Only a row's last tile has elements past the end, so full tiles take a
             // copy of the loop without the bounds test.
+            // (8-byte keys and wide rows rank item by item: the pipelined
+            // rank's extra live registers make them spill)
             auto rank_items = [&](auto partial) {
-#pragma unroll
-                for (int j = 0; j < ITEMS; ++j) {
-                    const uint32_t dig = reg_digit(key[j]);
-                    const uint32_t d = (decltype(partial)::value && elem(j) >= valid) ? (R - 1u) : dig;
-                    uint32_t below, size;
-                    group_rank(match_mask<B>(d), below, size);
-                    const uint32_t before = s_cnt[wave][d];
-                    rank[j] = (d << 16) | (before + below);
-                    pin(rank[j]);
-                    if (below == 0u) s_cnt[wave][d] = before + size;
-                }
+                wave_rank<B, ITEMS, sizeof(Word) == 4 && !kWide>(
+                    [&](int j) {
+                        const uint32_t dig = reg_digit(key[j]);
+                        return (decltype(partial)::value && elem(j) >= valid) ? (R - 1u) : dig;
+                    },
+                    s_cnt[wave], [&](int j, uint32_t d, uint32_t r) {
+                        rank[j] = (d << 16) | r;
+                        pin(rank[j]);
+                    });
             };
             if (valid == TILE) rank_items(std::false_type{});
             else rank_items(std::true_type{});
@@ -1005,17 +1054,15 @@ __global__ __launch_bounds__(BLOCK) void resident_sort_kernel(ResidentArgs a) {
         __syncthreads();
 
         uint32_t rank[ITEMS];
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t p = wbase + j * kWave + lane;
-            const uint32_t d = (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip, a.flip_neg) >> shift) & mask) : (R - 1u);
-            uint32_t below, size;
-            group_rank(match_mask<B>(d), below, size);
-            const uint32_t before = s_cnt[wave][d];
-            rank[j] = (d << 16) | (before + below);
-            pin(rank[j]);
-            if (below == 0u) s_cnt[wave][d] = before + size;
-        }
+        wave_rank<B, ITEMS, true>(
+            [&](int j) {
+                const uint32_t p = wbase + j * kWave + lane;
+                return (p < n) ? ((KeyTraits<KK>::key(key[j], a.flip, a.flip_neg) >> shift) & mask) : (R - 1u);
+            },
+            s_cnt[wave], [&](int j, uint32_t d, uint32_t r) {
+                rank[j] = (d << 16) | r;
+                pin(rank[j]);
+            });
         __syncthreads();
 
         uint32_t count = 0u;
@@ -1156,16 +1203,11 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_ROW_W
             }
 
             uint32_t rank[ITEMS];  // rank within the wave's digit
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t d = __builtin_amdgcn_ubfe(w[j], 16u + shift, B);
-                uint32_t below, size;
-                group_rank(match_mask<B>(d), below, size);
-                const uint32_t before = s_cnt[t][wave][d];
-                rank[j] = before + below;
-                pin(rank[j]);
-                if (below == 0u) s_cnt[t][wave][d] = before + size;
-            }
+            wave_rank<B, ITEMS, true>([&](int j) { return __builtin_amdgcn_ubfe(w[j], 16u + shift, B); }, s_cnt[t][wave],
+                                [&](int j, uint32_t, uint32_t r) {
+                                    rank[j] = r;
+                                    pin(rank[j]);
+                                });
             __syncthreads();
 
             // Digit d is owned by thread d: per-wave counts become per-wave
