@@ -50,14 +50,14 @@ KERNEL_SOURCES = ("lsd_radix_sort_amd/csrc/lrs_kernels.h", "lsd_radix_sort_amd/c
 # keyed by workload, with the hash of KERNEL_SOURCES the counters were taken
 # on.  A workload whose kernels have changed since reports traffic null.
 MEASURED_TRAFFIC = {
-    HEADLINE: {"kernel_sha16": "4c9af3a625d1359a", "bytes_per_launch": 4_455_526_368,
+    HEADLINE: {"kernel_sha16": "12070adfe5b63843", "bytes_per_launch": 4_455_888_743,
                "source": "profiles/sweep_kernel_2p28_pairs_uniform_hbm_traffic.md"},
     # the mean over the four passes' launches
-    "c4_fp16_1024x65536_asc": {"kernel_sha16": "4c9af3a625d1359a", "bytes_per_launch": 607_625_826,
+    "c4_fp16_1024x65536_asc": {"kernel_sha16": "12070adfe5b63843", "bytes_per_launch": 607_582_316,
                                "source": "profiles/sweep_kernel_fp16_1024x65536_asc_kernel_trace.md"},
-    "c5_bf16_4096x4096_desc": {"kernel_sha16": "4c9af3a625d1359a", "bytes_per_launch": 201_425_939,
+    "c5_bf16_4096x4096_desc": {"kernel_sha16": "12070adfe5b63843", "bytes_per_launch": 201_426_119,
                                "source": "profiles/row_resident_kernel_bf16_4096x4096_desc_kernel_trace.md"},
-    "i32_keys_2p28_asc": {"kernel_sha16": "4c9af3a625d1359a", "bytes_per_launch": 2_253_236_486,
+    "i32_keys_2p28_asc": {"kernel_sha16": "12070adfe5b63843", "bytes_per_launch": 2_252_930_642,
                           "source": "profiles/sweep_kernel_2p28_i32_keys_kernel_trace.md"},
 }
 
@@ -242,6 +242,55 @@ def graph_sweep(sizes, digit_bits: int, reps: int):
     return rows
 
 
+def tile_trace_report(rec, sweeps: int, clock_mhz: float, sweep_ms: float):
+    """Phase times of the sweep tiles of one sort from the library's tile
+    records (rec: int64 array [sweeps * tiles, 12], launches in order).
+    Prints a table per launch to stderr and returns a summary dict."""
+    import numpy as np
+
+    names = ["load + rank", "local scans", "reorder + look-back", "key write-out issue",
+             "payload load + reorder", "payload write-out issue"]
+    tiles = rec.shape[0] // sweeps
+    out = {"tiles_per_launch": int(tiles), "launches": []}
+    us = 1.0 / clock_mhz
+    log(f"{sweeps} sweep launches of {tiles} tiles; clock {clock_mhz:g} MHz")
+    log("| launch | span us | tile us (median) | " + " | ".join(f"{n} (median us)" for n in names) + " |")
+    log("|---:|---:|---:|" + "---:|" * len(names))
+    for L in range(sweeps):
+        r = rec[L * tiles:(L + 1) * tiles].astype(np.int64)
+        t = r[:, :7]
+        span = (t[:, 6].max() - t[:, 0].min()) * us
+        phases = np.diff(t, axis=1) * us
+        med = np.median(phases, axis=0)
+        lat = np.median(t[:, 6] - t[:, 0]) * us
+        out["launches"].append({"span_us": round(float(span), 1), "tile_us": round(float(lat), 2),
+                                "phase_median_us": [round(float(x), 2) for x in med],
+                                "phase_mean_us": [round(float(x), 2) for x in phases.mean(axis=0)]})
+        log(f"| {L} | {span:.1f} | {lat:.2f} | " + " | ".join(f"{x:.2f}" for x in med) + " |")
+    # where the tiles ran: the XCD each tile's workgroup reports against the
+    # XCD its index is dealt to (chunk c of 16 consecutive tiles to XCD c % 8)
+    r = rec[:tiles].astype(np.int64)
+    idx = np.arange(tiles)
+    xcc = r[:, 7] & 0xF
+    expect = (idx // 16) % 8
+    blk_xcd = r[:, 9] % 8
+    cu = (r[:, 8] >> 8) & 0xF
+    se = (r[:, 8] >> 13) & 0x7
+    places = np.unique(xcc * 1000 + se * 100 + cu).size
+    walk = rec[:, 10].astype(np.int64)
+    polls = rec[:, 11].astype(np.int64)
+    out.update({"tiles_on_dealt_xcd": int((xcc == expect).sum()), "workgroup_xcd_is_index_mod_8": int((xcc == blk_xcd).sum()),
+                "distinct_xcd_se_cu": int(places), "sweep_ms_timer": sweep_ms,
+                "lookback_predecessors_median": float(np.median(walk)), "lookback_predecessors_p90": float(np.percentile(walk, 90)),
+                "lookback_polls_median": float(np.median(polls)), "lookback_polls_p90": float(np.percentile(polls, 90))})
+    log(f"look-back of digit 0: predecessors added up median {np.median(walk):g} (p90 {np.percentile(walk, 90):g}), "
+        f"polls median {np.median(polls):g} (p90 {np.percentile(polls, 90):g})")
+    log(f"launch 0: {out['tiles_on_dealt_xcd']} of {tiles} tiles ran on the XCD their index is dealt to; "
+        f"XCD = workgroup index mod 8 for {out['workgroup_xcd_is_index_mod_8']}; "
+        f"{places} distinct (XCD, shader engine, CU) places")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +305,11 @@ def main():
     ap.add_argument("--graph-sweep", action="store_true",
                     help="instead of the workload: eager vs HIP-graph replay per-sort time of u32 keys-only "
                          "sorts from 1K to 1M keys (table on stderr, one JSON line)")
+    ap.add_argument("--tile-trace", action="store_true",
+                    help="after the warm-up, one sort with the tile phase records of a library built with "
+                         "-DLRS_TILE_TRACE=1 (pass it with --lib); phase table on stderr, one JSON line")
+    ap.add_argument("--tile-trace-out", default=None,
+                    help="with --tile-trace: also save the raw records (int64 [launches * tiles, 12]) as .npy")
     ap.add_argument("--lib", default=None,
                     help="library file to time instead of the in-tree build (a variant built with "
                          "python -m lsd_radix_sort_amd.build -D... --out PATH)")
@@ -379,6 +433,38 @@ def main():
     for _ in range(args.warmup):
         step(untimed)
     torch.cuda.synchronize()
+
+    if args.tile_trace:
+        # one more sort with every sweep tile's phase record; the clock rate
+        # is checked against the sweep time the kernel timer gives
+        buf = torch.zeros(max(1, n_keys // 2048) * lrs.KernelTimer.TRACE_WORDS * 8, dtype=torch.int64, device=dev)
+        try:
+            timer.trace_tiles(buf)
+        except lrs.RadixSortArgumentError:
+            log("this library records no tile phases: build one with python -m lsd_radix_sort_amd.build "
+                "-DLRS_TILE_TRACE=1 --out PATH and pass --lib PATH")
+            sys.exit(2)
+        with timer as kt:
+            step(timed)
+            torch.cuda.synchronize()
+        used = timer.trace_used()
+        timer.trace_tiles(None)
+        sweeps = kt.launches["sweep"]
+        if used == 0 or sweeps == 0:
+            log("no tile records: a library built with -DLRS_TILE_TRACE=1 and a workload sorted by sweeps are needed")
+            sys.exit(2)
+        rec = buf[:used].view(-1, lrs.KernelTimer.TRACE_WORDS).cpu().numpy()
+        if args.tile_trace_out:
+            np.save(args.tile_trace_out, rec)
+        first, last = rec[:, 0].min(), rec[:, 6].max()
+        sweep_ms = kt.ms["sweep"]
+        clock_mhz = 100.0
+        log(f"records span {(last - first) / clock_mhz:.1f} us at {clock_mhz:g} MHz; the timer's sweeps sum to "
+            f"{sweep_ms * 1e3:.1f} us")
+        summary = tile_trace_report(rec, sweeps, clock_mhz, sweep_ms)
+        print(json.dumps({"metric": "sweep tile phase times", "unit": "us", "workload": name, **summary}),
+              flush=True)
+        return
 
     log(f"timing {args.steps} steps")
     with timer as kt:

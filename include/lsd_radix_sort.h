@@ -287,6 +287,36 @@ lrs_timer *radix_sort_timer_create(void);
 int radix_sort_timer_read(lrs_timer *timer, double *ms_by_kind, int *launches_by_kind);
 void radix_sort_timer_destroy(lrs_timer *timer);
 
+/*
+ * Tile phase records for measurement, in libraries built with LRS_TILE_TRACE=1
+ * (python -m lsd_radix_sort_amd.build -DLRS_TILE_TRACE=1 --out PATH); the
+ * default build returns LRS_ERR_OPTION from radix_sort_timer_trace_tiles and
+ * records nothing.  The phases are those of one tile of a sweep pass with a
+ * decoupled look-back (CUDA Handbook ch.16: the per-block counting, scan and
+ * scatter of a pass; FlagTree PR #1084 step 2: the status look-back).
+ *
+ * radix_sort_timer_trace_tiles(timer, buf, words) gives the timer a device
+ * buffer of `words` 64-bit words (8-byte aligned, owned by the caller, which
+ * keeps it alive while calls record into it; buf NULL and words 0 detach it)
+ * and restarts its count.  Every later look-back sweep launch of an eager call
+ * timed by this timer takes the next num_tiles * LRS_TILE_TRACE_WORDS words
+ * while the buffer has room (launches that find no room record nothing), and
+ * each tile's first thread writes its record there: words 0-6 the GPU's
+ * 100 MHz real-time clock at the tile's start, after the rank, after the local
+ * scans, once its output offsets are known (look-back done, tile reordered),
+ * after issuing the key write-out, once the payload is in LDS and after issuing
+ * the payload write-out (keys-only passes repeat the key write-out time in
+ * words 5 and 6); word 7 the XCD id, word 8 the HW_ID register (CU in bits
+ * 8-11, shader engine in bits 13-15), word 9 the workgroup index, word 10 the
+ * number of predecessor tiles whose counts digit 0's look-back added up, word
+ * 11 the polls it spent waiting for a predecessor to publish.  Tile t of a
+ * launch is record t, tiles numbered row-major.
+ * radix_sort_timer_trace_used stores the words taken since the buffer was set.
+ */
+#define LRS_TILE_TRACE_WORDS 12
+int radix_sort_timer_trace_tiles(lrs_timer *timer, uint64_t *buf, uint64_t words);
+int radix_sort_timer_trace_used(const lrs_timer *timer, uint64_t *words);
+
 /* Static description of a status code; never NULL. */
 const char *radix_sort_status_string(int status);
 

@@ -103,6 +103,8 @@ def load_library():
         "radix_sort_timer_create": ([], P),
         "radix_sort_timer_read": ([P, P, P], c_int),
         "radix_sort_timer_destroy": ([P], None),
+        "radix_sort_timer_trace_tiles": ([P, P, u64], c_int),
+        "radix_sort_timer_trace_used": ([P, P], c_int),
         "radix_sort_status_string": ([c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
@@ -154,6 +156,26 @@ class KernelTimer:
         nl = (ctypes.c_int * 5)()
         _check(self._lib.radix_sort_timer_read(self.handle, ms, nl), "radix_sort_timer_read")
         return dict(zip(self.KINDS, list(ms))), dict(zip(self.KINDS, list(nl)))
+
+    TRACE_WORDS = 12  # LRS_TILE_TRACE_WORDS: one tile's phase record
+
+    def trace_tiles(self, buf: "torch.Tensor | None") -> None:
+        """Give the timer a device buffer (int64, contiguous) for tile phase
+        records, or None to detach it (libraries built with LRS_TILE_TRACE=1;
+        others raise RadixSortArgumentError)."""
+        if buf is None:
+            _check(self._lib.radix_sort_timer_trace_tiles(self.handle, None, 0), "radix_sort_timer_trace_tiles")
+            return
+        if not buf.is_cuda or buf.dtype != torch.int64 or not buf.is_contiguous():
+            _bad("trace buffer must be a contiguous int64 GPU tensor")
+        _check(self._lib.radix_sort_timer_trace_tiles(self.handle, _ptr(buf), buf.numel()),
+               "radix_sort_timer_trace_tiles")
+
+    def trace_used(self) -> int:
+        """Words of the trace buffer taken since it was set."""
+        w = ctypes.c_uint64(0)
+        _check(self._lib.radix_sort_timer_trace_used(self.handle, ctypes.byref(w)), "radix_sort_timer_trace_used")
+        return w.value
 
     def __enter__(self):
         self.read()  # start empty

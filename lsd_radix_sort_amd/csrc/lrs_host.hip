@@ -25,6 +25,11 @@ struct lrs_timer {
     std::vector<hipEvent_t> pool;  // pairs: start, stop
     std::vector<int> kind;
     size_t used = 0;
+    // tile phase records (builds with LRS_TILE_TRACE): the caller's device
+    // buffer, its size and the words handed out so far
+    uint64_t *trace = nullptr;
+    uint64_t trace_words = 0;
+    uint64_t trace_used = 0;
 };
 
 namespace lrs {
@@ -414,8 +419,17 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     return e;
 }
 
-SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass, const Ctx &c) {
+// `traced`: a look-back sweep, which records its tiles' phases in builds
+// with LRS_TILE_TRACE when the call's timer has a trace buffer with room.
+SweepArgs pass_args(const Plan &p, uint8_t *ws, int pass, const Ctx &c, bool traced = true) {
     SweepArgs a{};
+    if (LRS_TILE_TRACE && traced && c.timer != nullptr && c.timer->trace != nullptr) {
+        const uint64_t need = p.num_tiles * static_cast<uint64_t>(kTraceWords);
+        if (c.timer->trace_used + need <= c.timer->trace_words) {
+            a.trace = c.timer->trace + c.timer->trace_used;
+            c.timer->trace_used += need;
+        }
+    }
     const uint64_t R = 1ull << p.b;
     a.bases = reinterpret_cast<const uint32_t *>(ws + p.off_bases) + static_cast<uint64_t>(pass) * R;
     a.bases_row_stride = static_cast<uint32_t>(p.passes * R);
@@ -493,7 +507,7 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
     const uint32_t *src_k = keys_in;
     const uint32_t *src_v = vals_in;
     for (int pass = 0; pass < p.passes; ++pass) {
-        SweepArgs a = pass_args(p, ws, pass, c);
+        SweepArgs a = pass_args(p, ws, pass, c, false);
         PartArgs pa{};
         pa.keys = src_k;
         pa.counts = counts;
@@ -986,6 +1000,25 @@ int radix_sort_timer_read(lrs_timer *timer, double *ms_by_kind, int *launches_by
         if (ms_by_kind) ms_by_kind[k] += ms;
         if (launches_by_kind) launches_by_kind[k] += 1;
     }
+    return LRS_OK;
+}
+
+static_assert(lrs::kTraceWords == LRS_TILE_TRACE_WORDS, "trace record size as declared");
+
+int radix_sort_timer_trace_tiles(lrs_timer *timer, uint64_t *buf, uint64_t words) {
+    if (timer == nullptr) return LRS_ERR_NULL_POINTER;
+    if (!LRS_TILE_TRACE) return LRS_ERR_OPTION;  // a build without the records
+    if (buf == nullptr && words != 0) return LRS_ERR_NULL_POINTER;
+    if (misaligned(buf, 8)) return LRS_ERR_ALIGNMENT;
+    timer->trace = buf;
+    timer->trace_words = buf != nullptr ? words : 0;
+    timer->trace_used = 0;
+    return LRS_OK;
+}
+
+int radix_sort_timer_trace_used(const lrs_timer *timer, uint64_t *words) {
+    if (timer == nullptr || words == nullptr) return LRS_ERR_NULL_POINTER;
+    *words = timer->trace_used;
     return LRS_OK;
 }
 

@@ -50,6 +50,9 @@ namespace lrs {
 #ifndef LRS_PAYLOAD_EARLY
 #define LRS_PAYLOAD_EARLY 2     // payload loads before the key write-out: 0 never, 1 always, 2 for 8-byte keys
 #endif
+#ifndef LRS_TILE_TRACE
+#define LRS_TILE_TRACE 0        // measurement builds: look-back sweep tiles record their phase times
+#endif
 #ifndef LRS_RANK_PIPELINE
 #define LRS_RANK_PIPELINE 1     // ballot rank builds item j+1's match mask while item j's counter read is in flight
 #endif
@@ -386,6 +389,23 @@ struct SweepArgs {
     // of digit d).
     const uint32_t *part_offsets;
     uint32_t part_tiles;
+    // Builds with LRS_TILE_TRACE: kTraceWords words per tile of this launch
+    // (look-back mode), or NULL; unused otherwise.
+    uint64_t *trace;
+};
+
+// A tile's trace record: the 100 MHz real-time clock read by thread 0 at the
+// start, after the rank, after the local scans, once the offsets are known
+// (look-back done, tile reordered), after issuing the key write-out, after the
+// payload is in LDS and after issuing the payload write-out (keys-only passes
+// repeat the key write-out time), then the XCD id, the HW_ID register
+// (CU in bits 8-11, shader engine in 13-15), the workgroup index, and for
+// digit 0 the number of predecessors its look-back added up and the polls it
+// spent waiting for one to publish.
+constexpr int kTraceWords = 12;
+enum TraceSlot : int {
+    kTrStart = 0, kTrRanked = 1, kTrScanned = 2, kTrOffsets = 3, kTrKeysOut = 4, kTrPayIn = 5, kTrEnd = 6,
+    kTrXcc = 7, kTrHwId = 8, kTrBlock = 9, kTrWalk = 10, kTrPolls = 11
 };
 
 // Workgroup-wide exclusive scan of one value per thread for a BLOCK-thread
@@ -642,6 +662,22 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
         const uint32_t valid = min(TILE, a.row_len - tile_start);
         const uint64_t row_base = static_cast<uint64_t>(row) * a.row_len;
 
+        // (measurement builds only: thread 0 records the tile's phase times)
+        auto stamp = [&](int slot) {
+            if constexpr (LRS_TILE_TRACE && !PART) {
+                if (a.trace != nullptr && tid == 0)
+                    a.trace[static_cast<uint64_t>(t) * kTraceWords + slot] = __builtin_amdgcn_s_memrealtime();
+            }
+        };
+        if constexpr (LRS_TILE_TRACE && !PART) {
+            if (a.trace != nullptr && tid == 0) {
+                uint64_t *rec = a.trace + static_cast<uint64_t>(t) * kTraceWords;
+                rec[kTrXcc] = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20));   // XCC_ID
+                rec[kTrHwId] = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 4));  // HW_ID
+                rec[kTrBlock] = blockIdx.x;
+            }
+        }
+        stamp(kTrStart);
         const Stored *kin = static_cast<const Stored *>(a.keys_in) + row_base + tile_start;
         const uint32_t wbase = static_cast<uint32_t>(wave) * kWave * ITEMS;
         const __amdgpu_buffer_rsrc_t kin_rsrc = make_rsrc(kin, valid * sizeof(Stored));
@@ -696,7 +732,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             else
                 thread_count_digits<R, ITEMS, BLOCK>(
                     [&](int j) { return elem(j) >= valid ? R - 1u : reg_digit(key[j]); }, rank, cnt, tid);
+            stamp(kTrRanked);
             thread_counts_to_slots<R, ITEMS, BLOCK>(rank, cnt, s_tmp, tid, lane, wave, count, local_start);
+            stamp(kTrScanned);
         } else {
             // 2. Stable rank inside the wave; the group's lowest lane advances the
             // wave's running count of the digit.
@@ -718,6 +756,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             if (valid == TILE) rank_items(std::false_type{});
             else rank_items(std::true_type{});
             __syncthreads();
+            stamp(kTrRanked);
 
             // 3. Digit d is owned by thread d.
             if (tid < static_cast<int>(R)) {
@@ -743,6 +782,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                 for (int w = 0; w < WAVES; ++w) s_cnt[w][tid] += local_start;
             }
             __syncthreads();
+            stamp(kTrScanned);
 
             // 4. Local reorder: every key to its slot.
 #pragma unroll
@@ -824,6 +864,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                 s_goff[tid] = bucket_base + static_cast<uint32_t>(prefix) - local_start;
                 if (a.status_next != nullptr) static_cast<W *>(a.status_next)[static_cast<uint64_t>(t) * R + tid] = 0;
             };
+            if constexpr (LRS_TILE_TRACE) {
+                if (a.trace != nullptr && tid == 0) {
+                    a.trace[static_cast<uint64_t>(t) * kTraceWords + kTrWalk] = back - 1u;
+                    a.trace[static_cast<uint64_t>(t) * kTraceWords + kTrPolls] = polls;
+                }
+            }
             if (gave_up && lane == 0) s_gave_up = 1u;
             if (!from_keys && !gave_up && tid < static_cast<int>(R)) finish(excl);
             __syncthreads();
@@ -842,6 +888,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             }
         }
         if constexpr (PART) __syncthreads();
+        stamp(kTrOffsets);
 
         // 5. Keys out: slot k goes to s_goff[d] + k.  That is below row_len for
         // every real element; the range check of the buffer store only keeps a
@@ -915,6 +962,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
             if (valid == TILE) keys_out(std::false_type{}, std::false_type{});
             else keys_out(std::true_type{}, std::false_type{});
         }
+        stamp(kTrKeysOut);
 
         // Otherwise the payload is loaded only now, after the keys have gone out
         // (loading it before the look-back, to overlap that wait, measured 0.3%
@@ -936,6 +984,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                 s_pay[rank[j]] = v;
             }
             __syncthreads();
+            stamp(kTrPayIn);
             using OutT = typename std::conditional<PK == kPayIdxLast, int64_t, uint32_t>::type;
             OutT *vout = static_cast<OutT *>(a.vals_out) + row_base;
             const __amdgpu_buffer_rsrc_t vout_rsrc = make_rsrc(vout, kWide ? 0u : a.row_len * sizeof(OutT));
@@ -967,6 +1016,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(LRS_SWEEP
                 }
             }
         }
+        if constexpr (!kPayPhase) stamp(kTrPayIn);
+        stamp(kTrEnd);
         if constexpr (PART) {
             // the next tile reuses the LDS: counters cleared, every read of this tile done
             __syncthreads();

@@ -206,3 +206,20 @@ def test_python_binding_rejects_bad_outputs_and_workspace():
         lrs.check_workspace(torch.empty(100, dtype=torch.int32), cpu, 4)
     with pytest.raises(ValueError, match="is on cpu"):
         lrs.check_workspace(ws, torch.device("cuda:0"), 4)
+
+
+def test_tile_trace_entry_points_in_the_default_build():
+    # the phase records exist only in builds with LRS_TILE_TRACE=1; the default
+    # library exports the entry points, refuses a trace buffer and records nothing
+    lib = lrs.load_library()
+    t = lib.radix_sort_timer_create()
+    assert t
+    try:
+        used = ctypes.c_uint64(7)
+        assert lib.radix_sort_timer_trace_tiles(None, None, 0) == 1      # LRS_ERR_NULL_POINTER
+        assert lib.radix_sort_timer_trace_tiles(t, None, 0) == 10        # LRS_ERR_OPTION: not a trace build
+        assert lib.radix_sort_timer_trace_used(None, ctypes.byref(used)) == 1
+        assert lib.radix_sort_timer_trace_used(t, None) == 1
+        assert lib.radix_sort_timer_trace_used(t, ctypes.byref(used)) == 0 and used.value == 0
+    finally:
+        lib.radix_sort_timer_destroy(t)
