@@ -68,3 +68,36 @@ def test_traffic_is_tied_to_the_kernel_sources(monkeypatch):
     monkeypatch.setattr(bench, "MEASURED_TRAFFIC", {"x": {"kernel_sha16": "0" * 16, "bytes_per_launch": 123,
                                                           "source": "test"}})
     assert bench.measured_traffic("x") is None
+
+
+def test_tile_trace_report_phases_and_placement():
+    # two launches of 32 tiles, records built by hand: phase k of every tile
+    # lasts k + 1 ticks of the 100 MHz clock (10 ns), launch 1 starts 1000
+    # ticks later, tile t of launch 0 ran on XCD (t // 16) % 8 (the dealing of
+    # chunks of 16), tile 5 of it on a wrong one
+    import numpy as np
+
+    tiles, sweeps = 32, 2
+    rec = np.zeros((sweeps * tiles, 12), dtype=np.int64)
+    for L in range(sweeps):
+        for t in range(tiles):
+            r = rec[L * tiles + t]
+            r[0] = 1000 * L + t
+            for k in range(6):
+                r[k + 1] = r[k] + (k + 1)
+            r[7] = (t // 16) % 8
+            r[8] = (t % 4) << 8 | (t % 2) << 13   # CU, shader engine
+            r[9] = 8 * t + (t // 16) % 8           # a workgroup index on that XCD
+            r[10] = 3
+            r[11] = 0
+    rec[5, 7] = 7
+    out = bench.tile_trace_report(rec, sweeps, 100.0, 0.5)
+    assert out["tiles_per_launch"] == tiles and len(out["launches"]) == sweeps
+    for launch in out["launches"]:
+        assert launch["phase_median_us"] == [0.01, 0.02, 0.03, 0.04, 0.05, 0.06]
+        assert launch["tile_us"] == 0.21
+        assert launch["span_us"] == round((31 + 21) / 100.0, 1)
+    assert out["tiles_on_dealt_xcd"] == tiles - 1
+    # tile 5 reported XCD 7, not its workgroup index mod 8
+    assert out["workgroup_xcd_is_index_mod_8"] == tiles - 1
+    assert out["lookback_predecessors_median"] == 3.0 and out["lookback_polls_median"] == 0.0
