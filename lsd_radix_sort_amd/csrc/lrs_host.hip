@@ -136,11 +136,12 @@ int choose_tile_cfg(uint64_t rows, uint64_t row_len, bool key64, bool keys_only)
 }
 constexpr uint64_t kAlign = 256;
 #ifndef LRS_HIST_BLOCKS
-#define LRS_HIST_BLOCKS 512
+#define LRS_HIST_BLOCKS 256
 #endif
 // Histogram workgroups per launch: 1024 threads and 128 KB of LDS counters
-// each, so one per CU at a time (measured on 2^28 keys against 256 and, with
-// smaller workgroups and fewer copies, 640 to 5120).
+// each, so one per CU at a time, and 256 of them fill the GPU once (one round
+// of long spans; 512 and 1024 workgroups, two and four rounds, measured
+// slower on 2^27 and 2^28 keys, as did smaller workgroups with fewer copies).
 constexpr uint32_t kHistTargetBlocks = LRS_HIST_BLOCKS;
 #ifndef LRS_HIST_MIN_CHUNK
 #define LRS_HIST_MIN_CHUNK 16384
