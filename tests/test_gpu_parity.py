@@ -377,8 +377,9 @@ def test_c5_bf16_4096x4096_descending():
     assert_same(gi.ravel(), ei.ravel(), "c5 indices")
 
 
-@pytest.mark.parametrize("rows,n", [(1, 1), (3, 7), (5, 4095), (2, 4097), (3, 8192), (3, 8193), (7, 12345),
-                                     (3, 65535), (2, 65536), (2, 65537), (1, 70000), (300, 33), (2, 200_000)])
+@pytest.mark.parametrize("rows,n", [(1, 1), (3, 7), (4, 1000), (2, 2048), (5, 4095), (2, 4097), (3, 8192),
+                                     (3, 8193), (7, 12345), (3, 65535), (2, 65536), (2, 65537), (1, 70000),
+                                     (300, 33), (2, 200_000)])
 @pytest.mark.parametrize("b", [1, 2, 4, 8])
 def test_rows_ragged_shapes(rows, n, b):
     bits = workloads.fp16_normal_bits(rows * 131 + n, rows * n).reshape(rows, n)
