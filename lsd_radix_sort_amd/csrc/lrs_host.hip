@@ -413,6 +413,7 @@ hipError_t launch_histogram(const Plan &p, const void *keys, uint32_t *hist, int
     const uint32_t blocks = static_cast<uint32_t>(p.rows * p.hist_chunks_per_row);
     TimedLaunch t(1, c);
     hipError_t e = (kk == kKeyU32)   ? launch_hist<kKeyU32>(p.b, h, blocks, t.L)
+                   : (kk == kKeyC32) ? launch_hist<kKeyC32>(p.b, h, blocks, t.L)
                    : (kk == kKeyX32) ? launch_hist<kKeyX32>(p.b, h, blocks, t.L)
                    : (kk == kKeyU64) ? launch_hist<kKeyU64>(p.b, h, blocks, t.L)
                    : (kk == kKeyX64) ? launch_hist<kKeyX64>(p.b, h, blocks, t.L)
@@ -458,14 +459,15 @@ T *pass_dst(int pass, int passes, T *out, T *alt) {
 
 // Kernel key kind and transform masks of a (key type, direction); false for an
 // unknown key type.  The masks give each type's order-preserving u32 image and
-// complement it for descending order (see KeyTraits<kKeyX32>).
+// complement it for descending order (see KeyTraits<kKeyX32>); where both masks
+// are equal (signed integers, descending u32) the image is one XOR (kKeyC32).
 bool key_transform(int key_type, int descending, int &kk, uint64_t &flip, uint64_t &flip_neg) {
     const uint64_t c = descending ? ~0ull : 0ull;
     const uint64_t c32 = c & 0xFFFFFFFFull;
     const uint64_t top64 = 1ull << 63;
     switch (key_type) {
-        case LRS_KEY_U32: kk = descending ? kKeyX32 : kKeyU32; flip = c32; flip_neg = c32; return true;
-        case LRS_KEY_I32: kk = kKeyX32; flip = 0x80000000ull ^ c32; flip_neg = 0x80000000ull ^ c32; return true;
+        case LRS_KEY_U32: kk = descending ? kKeyC32 : kKeyU32; flip = c32; flip_neg = c32; return true;
+        case LRS_KEY_I32: kk = kKeyC32; flip = 0x80000000ull ^ c32; flip_neg = 0x80000000ull ^ c32; return true;
         case LRS_KEY_F32: kk = kKeyX32; flip = 0x80000000ull ^ c32; flip_neg = 0xFFFFFFFFull ^ c32; return true;
         case LRS_KEY_U64: kk = descending ? kKeyX64 : kKeyU64; flip = c; flip_neg = c; return true;
         case LRS_KEY_I64: kk = kKeyX64; flip = top64 ^ c; flip_neg = top64 ^ c; return true;
@@ -521,8 +523,9 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
         pa.flip_neg = flip_neg;
         {
             TimedLaunch t(1, c);
-            const hipError_t e = (kk == kKeyU32) ? launch_partition_counts<kKeyU32>(p.b, pa, t.L)
-                                                 : launch_partition_counts<kKeyX32>(p.b, pa, t.L);
+            const hipError_t e = (kk == kKeyU32)   ? launch_partition_counts<kKeyU32>(p.b, pa, t.L)
+                                 : (kk == kKeyC32) ? launch_partition_counts<kKeyC32>(p.b, pa, t.L)
+                                                   : launch_partition_counts<kKeyX32>(p.b, pa, t.L);
             if (e != hipSuccess) return LRS_ERR_HIP;
         }
         uint32_t *dk = pass_dst(pass, p.passes, keys_out, alt_k);
@@ -538,12 +541,14 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
-                                : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L);
+            e = (kk == kKeyU32)   ? launch_sweep<kKeyU32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
+                : (kk == kKeyC32) ? launch_sweep<kKeyC32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
+                                  : launch_sweep<kKeyX32, kPayU32, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
-                                : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L);
+            e = (kk == kKeyU32)   ? launch_sweep<kKeyU32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
+                : (kk == kKeyC32) ? launch_sweep<kKeyC32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L)
+                                  : launch_sweep<kKeyX32, kPayNone, true>(p.b, a, p.tile_cfg, p.wide_status, partitions, t.L);
         }
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;
@@ -552,7 +557,7 @@ int sort_32_reduce_then_scan(const Plan &p, int kk, uint64_t flip, uint64_t flip
 }
 
 // Keys of 32 bits: u32 as they are (KK = kKeyU32), anything else through the
-// two-mask transform (KK = kKeyX32).
+// two-mask transform (KK = kKeyX32) or one constant XOR (KK = kKeyC32).
 int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t *keys_in,
             const uint32_t *vals_in, uint32_t *keys_out, uint32_t *vals_out, uint64_t n, int begin_bit,
             int end_bit, int b, void *workspace, size_t ws_bytes, void *stream, const lrs_options *opts) {
@@ -591,6 +596,8 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
         hipError_t e;
         if (kk == kKeyU32)
             e = pairs ? resident<kKeyU32, kResU32>(b, r, 1, n, c) : resident<kKeyU32, kResNone>(b, r, 1, n, c);
+        else if (kk == kKeyC32)
+            e = pairs ? resident<kKeyC32, kResU32>(b, r, 1, n, c) : resident<kKeyC32, kResNone>(b, r, 1, n, c);
         else
             e = pairs ? resident<kKeyX32, kResU32>(b, r, 1, n, c) : resident<kKeyX32, kResNone>(b, r, 1, n, c);
         return e == hipSuccess ? LRS_OK : LRS_ERR_HIP;
@@ -618,12 +625,14 @@ int sort_32(int kk, uint64_t flip, uint64_t flip_neg, bool pairs, const uint32_t
             uint32_t *dv = pass_dst(pass, p.passes, vals_out, alt_v);
             a.vals_in = src_v;
             a.vals_out = dv;
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
-                                : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
+            e = (kk == kKeyU32)   ? launch_sweep<kKeyU32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                : (kk == kKeyC32) ? launch_sweep<kKeyC32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                                  : launch_sweep<kKeyX32, kPayU32, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
             src_v = dv;
         } else {
-            e = (kk == kKeyU32) ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
-                                : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
+            e = (kk == kKeyU32)   ? launch_sweep<kKeyU32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                : (kk == kKeyC32) ? launch_sweep<kKeyC32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L)
+                                  : launch_sweep<kKeyX32, kPayNone, false>(b, a, p.tile_cfg, p.wide_status, p.num_tiles, t.L);
         }
         if (e != hipSuccess) return LRS_ERR_HIP;
         src_k = dk;

@@ -1,4 +1,4 @@
-// lrs_inst_x32_keys.hip -- other 32-bit keys (signed, float, descending u32), keys only
+// lrs_inst_x32_keys.hip -- 32-bit keys under the two-mask transform (floats), keys only
 // (the kernels of one key kind, compiled in their own translation unit).
 #include "lrs_launch_impl.h"
 

@@ -1,4 +1,4 @@
-// lrs_inst_x32_pairs.hip -- other 32-bit keys (signed, float, descending u32) with a u32 payload
+// lrs_inst_x32_pairs.hip -- 32-bit keys under the two-mask transform (floats) with a u32 payload
 // (the kernels of one key kind, compiled in their own translation unit).
 #include "lrs_launch_impl.h"
 

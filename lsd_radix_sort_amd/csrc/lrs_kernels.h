@@ -65,7 +65,7 @@ constexpr uint32_t kXcdChunk = LRS_XCD_CHUNK;
 constexpr uint32_t kXcds = 8;          // accelerator complex dies (XCDs) of an MI355X
 constexpr int kWave = 64;              // CDNA wavefront width
 
-enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1, kKeyX32 = 2, kKeyU64 = 3, kKeyX64 = 4 };
+enum KeyKind : int { kKeyU32 = 0, kKeyF16 = 1, kKeyX32 = 2, kKeyU64 = 3, kKeyX64 = 4, kKeyC32 = 5 };
 
 // Payload handling of one pass.
 enum PayKind : int {
@@ -117,6 +117,18 @@ template <> struct KeyTraits<kKeyX32> {
     // negatives).  Descending order complements both masks (u32: both ~0).
     __device__ static inline uint32_t key(uint32_t v, uint64_t flip, uint64_t flip_neg) {
         return v ^ static_cast<uint32_t>((static_cast<int32_t>(v) < 0) ? flip_neg : flip);
+    }
+};
+
+template <> struct KeyTraits<kKeyC32> {
+    using Stored = uint32_t;
+    using Word = uint32_t;
+    // 32-bit keys whose order-preserving image is the pattern XORed with one
+    // constant, whatever the sign bit: signed integers (0x80000000, and
+    // 0x7FFFFFFF descending) and descending u32 (0xFFFFFFFF).  One XOR, where
+    // kKeyX32's two masks take a compare and a select as well.
+    __device__ static inline uint32_t key(uint32_t v, uint64_t flip, uint64_t) {
+        return v ^ static_cast<uint32_t>(flip);
     }
 };
 
