@@ -49,24 +49,24 @@ def make_keys(key_type: str, n: int, seed: int) -> np.ndarray:
 
 
 def gpu_typed(bits: np.ndarray, key_type: str, descending: bool, b: int, with_vals: bool,
-              begin: int = 0, end: int = 32):
+              begin: int = 0, end: int = 32, options=None):
     kt = torch.from_numpy(bits.view(np.int32).copy()).cuda()
     if key_type == "f32":
         kt = kt.view(torch.float32)
     vals = np.arange(bits.size, dtype=np.uint32) * np.uint32(2654435761)
     if with_vals:
         vt = torch.from_numpy(vals.view(np.int32).copy()).cuda()
-        ko, vo = lrs.radix_sort_pairs_typed(kt, vt, descending, key_type, begin, end, b)
+        ko, vo = lrs.radix_sort_pairs_typed(kt, vt, descending, key_type, begin, end, b, options=options)
         torch.cuda.synchronize()
         return ko.view(torch.int32).cpu().numpy().view(np.uint32), vo.cpu().numpy().view(np.uint32), vals
-    ko = lrs.radix_sort_keys_typed(kt, descending, key_type, begin, end, b)
+    ko = lrs.radix_sort_keys_typed(kt, descending, key_type, begin, end, b, options=options)
     torch.cuda.synchronize()
     return ko.view(torch.int32).cpu().numpy().view(np.uint32), None, vals
 
 
-def check(bits, key_type, descending, b, begin=0, end=32):
+def check(bits, key_type, descending, b, begin=0, end=32, options=None):
     for with_vals in (False, True):
-        gk, gv, vals = gpu_typed(bits, key_type, descending, b, with_vals, begin, end)
+        gk, gv, vals = gpu_typed(bits, key_type, descending, b, with_vals, begin, end, options)
         ek, ev = oracle.radix_sort_typed(bits, vals if with_vals else None, key_type, descending, begin, end, b)
         bad = np.flatnonzero(gk != ek)
         assert bad.size == 0, f"{key_type} desc={descending} b={b} keys differ at {bad[:5]} (of {bad.size})"
@@ -100,6 +100,25 @@ def test_typed_bit_window():
     bits = make_keys("f32", 100_000, 5300)
     check(bits, "f32", False, 4, 20, 32)
     check(bits, "f32", True, 8, 16, 32)
+
+
+@pytest.mark.parametrize("key_type", ["i32", "u32"])
+def test_typed_one_xor_kinds(key_type):
+    # int32 keys (either direction) and descending u32 keys map to their image
+    # by one XOR with a constant: bit windows, narrow digits, the
+    # reduce-then-scan sweeps and the largest tile of that key kind
+    bits = make_keys(key_type, 200_003, 5500)
+    for descending in ((False, True) if key_type == "i32" else (True,)):
+        log(f"{key_type} desc={descending} windows")
+        check(bits, key_type, descending, 4, 20, 32)
+        check(bits, key_type, descending, 8, 8, 31)
+        log(f"{key_type} desc={descending} reduce-then-scan")
+        check(bits, key_type, descending, 8, options=lrs.SortOptions(scan="reduce-then-scan"))
+    for b in (1, 2):
+        check(bits[:50_003], key_type, True, b)
+    big = make_keys(key_type, 15_000_007, 5600)
+    log(f"{key_type} n=15000007 desc")
+    check(big, key_type, True, 8)
 
 
 def test_typed_largest_tile():
